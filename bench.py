@@ -1,0 +1,243 @@
+"""Throughput of the chunked gated-delta-rule prefill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3]
+
+One step = one gdn_prefill call (all three stages) over the whole synthetic
+workload, inputs resident in HBM.  Default workload: B=4 sequences of T=8192
+tokens, nk=16 k-heads, nv=32 v-heads, dk=dv=128, carried float32 state updated
+in place, per-chunk entry states emitted (the T=8192 workload the target is
+stated on).  Prints one JSON line.
+
+roofline: the dominant kernel's algorithmic bytes per launch (the byte model
+below, per token-head / per slot, times the units one launch processes) over
+its average launch time, timed live with HIP events on the launch stream.
+traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, read
+from profiles/traffic_<kernel>_<workload>.json when that file was taken on the
+current kernel source (its sha256 matches), else null.
+cpu_baseline: the oracle (float64 token recurrence) timed on the host cores
+over a bounded sample of the same workload's chains.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN chunked prefill tokens/sec on 1 MI355X; % bf16 MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, AMD published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+KERNELS = {1: "chunk_cumsum_recompute_wu", 2: "chunk_delta_h", 3: "chunk_fwd_o"}
+KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h.hip", 3: "k3_chunk_fwd_o.hip"}
+
+
+# ---------------------------------------------------------------------------
+# byte and flop model (algorithmic: every byte each stage must move once)
+
+
+def algorithmic(p):
+    """Per-kernel algorithmic bytes and flops for problem p (inputs.Problem)."""
+    N, nk, nv = p.n_tokens, p.nk, p.nv
+    slots = int(p.cu_chunks[-1]) * nv
+    nseq = p.nseq
+    d, C = 128, 64
+    k_bytes = N * nk * d * 2
+    q_bytes = N * nk * d * 2
+    v_bytes = N * nv * d * 2
+    gb_bytes = N * nv * 8
+    gc_bytes = slots * C * 4
+    wu_bytes = slots * C * d * 4 * 2
+    s_bytes = slots * d * d * 2
+    uc_bytes = slots * d * C * 2
+    state_bytes = nseq * nv * d * d * 4
+    o_bytes = N * nv * d * 2
+    by = {
+        1: k_bytes + v_bytes + gb_bytes + gc_bytes + wu_bytes,
+        2: wu_bytes + k_bytes + gc_bytes + 2 * state_bytes + s_bytes + uc_bytes,
+        3: q_bytes + k_bytes + gc_bytes + s_bytes + uc_bytes + o_bytes,
+    }
+    # dense-tile flops per chunk-head: Gram 2C^2 d, WY 2C^2 (dk+dv), spine 4 C d^2,
+    # output 2 C d^2 + 2 C^2 d + 2 C^2 d
+    fl = {1: slots * (2 * C * C * d + 2 * C * C * 2 * d),
+          2: slots * (4 * C * d * d),
+          3: slots * (2 * C * d * d + 4 * C * C * d)}
+    return by, fl
+
+
+def source_sha(stage):
+    path = os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", KERNEL_SRC[stage])
+    h = hashlib.sha256()
+    for f in (path, os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", "gdn_device.h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(stage, workload_name):
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNELS[stage]}_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_sha(stage):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample, forked workers (before the GPU
+# is touched)
+
+
+def _oracle_chain(args):
+    idx, i, h, tmax, seconds = args
+    from threadpoolctl import threadpool_limits
+    from oracle import gdn_recurrence, kv_head_map
+    from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64
+    p = _SAMPLE_PROBLEM
+    a = int(p.cu_seqlens[i])
+    L = min(int(p.lengths[i]), tmax)
+    kap = kv_head_map(p.nk, p.nv)[[h]]
+    q = bf16_to_f64(p.q[a:a + L][:, kap])
+    k = bf16_to_f64(p.k[a:a + L][:, kap])
+    v = bf16_to_f64(p.v[a:a + L][:, [h]])
+    g = p.g[a:a + L][:, [h]].astype("float64")
+    b = p.beta[a:a + L][:, [h]].astype("float64")
+    h0 = p.h0[i][[h]].astype("float64")
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        step = 256
+        while done < L and time.perf_counter() - t0 < seconds:
+            n = min(step, L - done)
+            _, h0, _ = gdn_recurrence(q[done:done + n], k[done:done + n], v[done:done + n],
+                                      g[done:done + n], b[done:done + n], h0)
+            done += n
+    return done, time.perf_counter() - t0
+
+
+_SAMPLE_PROBLEM = None
+
+
+def cpu_baseline(p, seconds_per_worker=1.5):
+    import multiprocessing as mp
+    global _SAMPLE_PROBLEM
+    _SAMPLE_PROBLEM = p
+    workers = max(1, min(16, os.cpu_count() or 1))
+    jobs = [(w, w % p.nseq, (7 * w) % p.nv, 8192, seconds_per_worker) for w in range(workers)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        res = pool.map(_oracle_chain, jobs)
+    wall = time.perf_counter() - t0
+    token_heads = sum(r[0] for r in res)
+    cpu_s = sum(r[1] for r in res)
+    return {
+        "value": token_heads / wall / p.nv,
+        "unit": "tokens/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{workers} (sequence, v-head) chains of this workload run through the float64 "
+                   f"token recurrence for ~{seconds_per_worker}s each ({token_heads} token-heads, "
+                   f"{cpu_s:.1f} core-s, wall {wall:.1f}s); tokens/s = token-heads/s / nv"),
+    }
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
+              f"requested); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from linear_attention_ssm_chunk_amd import inputs as I
+    p = I.make_workload(args.workload)
+    wname = p.meta["name"]
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(p)
+
+    import torch
+    from linear_attention_ssm_chunk_amd.device import DeviceProblem
+    kw = {}
+    if p.meta["layout"] == "conv":
+        kw = dict(layout="conv")
+    elif p.meta["layout"] == "varlen_table":
+        kw = dict(state="table", ragged=True)
+    dp = DeviceProblem(p, **kw)
+
+    for _ in range(args.warmup):
+        dp.run()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record()
+        dp.run_stage(1)
+        e[1].record()
+        dp.run_stage(2)
+        e[2].record()
+        dp.run_stage(3)
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {st: sum(ev[s][st - 1].elapsed_time(ev[s][st]) for s in range(args.steps)) / args.steps
+           for st in (1, 2, 3)}
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = p.n_tokens
+    value = tokens / (ms_per_step / 1e3)
+
+    by, fl = algorithmic(p)
+    dom = max(per, key=per.get)
+    achieved = by[dom] / (per[dom] / 1e3) / 1e9
+    kernels = {KERNELS[st]: {"ms": round(per[st], 4), "alg_bytes": by[st],
+                             "alg_GBps": round(by[st] / (per[st] / 1e3) / 1e9, 1),
+                             "hbm_frac": round(by[st] / (per[st] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "mfma_frac": round(fl[st] / (per[st] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+               for st in (1, 2, 3)}
+    total_bytes = sum(by.values())
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wname, "B": p.nseq, "T": max(p.lengths), "n_tokens": tokens, "nk": p.nk,
+                   "nv": p.nv, "dk": 128, "dv": 128, "chunk": 64, "global_batch": p.nseq,
+                   "seq_len": max(p.lengths), "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(dom, wname)},
+        "kernels": kernels,
+        "whole_step": {"alg_bytes": total_bytes,
+                       "alg_GBps": round(total_bytes / (ms_per_step / 1e3) / 1e9, 1),
+                       "mfma_frac": round(sum(fl.values()) / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * gdn_prefill.h -- C ABI of the MI355X (gfx950) chunked gated-delta-rule
+ * (Gated DeltaNet) prefill forward.
+ *
+ * The operation.  Per value head, over the tokens of each sequence,
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t                                    (no query scale)
+ * (Gated DeltaNet, Yang, Kautz & Hatamizadeh, ICLR 2025).  It is evaluated in
+ * 64-token chunks in the three stages the page
+ * "spark_model/layers/ops/ssm_gdn_a3.rs" lists in the doc comment of
+ * gdn_prefill_fla:
+ *   1. chunk_cumsum_recompute_wu: chunk-local cumulative log-gate gc, the
+ *      strictly lower L (sharing the key Gram), and the WY/UT solves
+ *      (I+L) W = beta exp(gc) K, (I+L) U = beta V;
+ *   2. chunk_delta_h: a serial float32 state spine over chunks that emits each
+ *      chunk's entry state and corrected values uc = U - W h, and leaves the
+ *      final state in place;
+ *   3. chunk_fwd_o: O = diag(exp(gc)) Q h_c + tril(decay * Q K^T) uc.
+ * The arguments follow that page's launcher (gdn_prefill_fla's parameter
+ * list): separate k/v head counts, packed strided rows, optional ragged
+ * cu_seqlens / cu_chunks, a per-request state pointer table, caller-owned
+ * scratch, one stream.
+ *
+ * Conventions.
+ *   - dk = dv = 128 and the chunk is 64 tokens (the kernels are specialised,
+ *     as the page's tile guard gdn_tc_spine_reject is); other sizes are
+ *     rejected with GDN_EUNSUPPORTED.
+ *   - GQA grouping: v-head h reads k-head (h * nk) / nv; nv % nk == 0.
+ *   - The state is stored h[dk][dv] (the page's "[nv,kd,vd]" h_state), the
+ *     transpose of S above.
+ *   - Tokens of a sequence occupy consecutive token rows.  Dense mode:
+ *     sequence b is rows b*T .. b*T+T-1.  Ragged mode: rows cu_seqlens[i] ..
+ *     cu_seqlens[i+1]-1.
+ *   - Element (row, head h, component d) of q / k is at
+ *     q[row*qk_row + kappa(h)*128 + d]; of v at v[row*v_row + h*128 + d];
+ *     g and beta at g[row*gb_row + h], beta[row*gb_row + h].  Strides are in
+ *     ELEMENTS.  q, k and v may point into one packed buffer (the page's conv
+ *     layout: qk_stride = v_stride = conv_dim, gb_stride = 2*nv).
+ *   - out is bf16 [N_tok][nv][dv], contiguous (N_tok = B*T, or cu_seqlens[B]).
+ *   - exp(gc) of the chunk-local gate must stay finite in float32 (gc < 88);
+ *     g <= 0 (a decay) always satisfies it, and any decay however strong is
+ *     handled (factors that underflow are 0, as they are in the result).
+ *
+ * Ownership.  The caller owns every buffer.  The library allocates nothing,
+ * keeps no pointer after return, and never reads device memory from the host.
+ * q, k, v, g, beta may alias each other (read-only).  out, scratch and the
+ * state must not alias the inputs or each other.
+ *
+ * Execution.  gdn_prefill enqueues three kernels on `stream` (a hipStream_t)
+ * and returns; there is no device synchronisation.  Asynchronous faults
+ * surface at the caller's next synchronisation.  Calls on different streams
+ * with disjoint outputs and scratch may run concurrently.
+ *
+ * Errors.  Every entry point returns GDN_OK (0) or a negative code;
+ * gdn_last_error() then names the guard that rejected the call (thread-local
+ * text).  There is no fallback path of any kind.
+ */
+#ifndef GDN_PREFILL_H
+#define GDN_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_CHUNK 64
+#define GDN_HEAD_DIM 128
+
+enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,       /* malformed argument (null pointer, bad stride, ...) */
+  GDN_EUNSUPPORTED = -2, /* head size / chunk other than 128 / 64            */
+  GDN_ESCRATCH = -3,     /* scratch_bytes smaller than gdn_prefill_scratch_bytes */
+  GDN_EHIP = -4          /* a HIP runtime call failed; message has its text  */
+};
+
+/* Token-row pitches in elements (the page's qk_stride, v_stride, gb_stride). */
+typedef struct gdn_strides {
+  int64_t qk_row; /* q and k rows (bf16 elements); multiple of 8 */
+  int64_t v_row;  /* v rows (bf16 elements); multiple of 8       */
+  int64_t gb_row; /* g and beta rows (float elements); >= nv     */
+} gdn_strides;
+
+/* Ragged co-dispatch (the page's VARLEN arguments).  Pass NULL for dense. */
+typedef struct gdn_varlen {
+  const int32_t *cu_seqlens; /* device, B+1 token offsets, cu_seqlens[0] = 0     */
+  const int32_t *cu_chunks;  /* device, B+1 chunk offsets,
+                                cu_chunks[i+1]-cu_chunks[i] = ceil(len_i / 64)   */
+  int32_t max_chunks;        /* host: max_i ceil(len_i / 64) (grid extent)       */
+  int32_t total_chunks;      /* host: cu_chunks[B] (sizes the scratch)           */
+} gdn_varlen;
+
+/*
+ * Scratch layout.  A "slot" is one (sequence, v-head, chunk):
+ *   slot(i, h, c) = cu_chunks[i]*nv + h*n_i + c,   n_i = chunks of sequence i
+ * (dense: cu_chunks[i] = i*ceil(T/64), so slots run [B][nv][n_chunks]).
+ * Regions (byte offsets from the scratch base, each 256-byte aligned):
+ *   gc      float [slots][64]        chunk-local cumulative log-gate; rows past
+ *                                    the sequence end repeat the last value
+ *   w       float [slots][64][128]   W (rows past the end are 0)
+ *   u       float [slots][64][128]   U (rows past the end are 0)
+ *   s_entry bf16  [slots][128][128]  entry state of each chunk, [dk][dv]; for
+ *                                    dense input this is [B][nv][T/64][dk][dv]
+ *   uc      bf16  [slots][128][64]   corrected values uc = U - W h, stored
+ *                                    transposed ([dv][token])
+ */
+typedef struct gdn_scratch_layout {
+  size_t gc, w, u, s_entry, uc; /* byte offsets */
+  size_t total;                 /* bytes needed */
+  int64_t slots;                /* chunk slots  */
+} gdn_scratch_layout;
+
+/* Scratch bytes for a problem (at least 256).  varlen NULL: dense B x T.
+ * Returns 0 if the sizes are invalid. */
+size_t gdn_prefill_scratch_bytes(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen);
+
+/* Fill *out with the scratch layout above.  Returns GDN_OK or an error. */
+int gdn_prefill_scratch_layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen,
+                               gdn_scratch_layout *out);
+
+/*
+ * Validate every argument of gdn_prefill without touching the GPU (pure host
+ * logic; pointer values are checked for NULL and 16-byte alignment only).
+ * Returns GDN_OK or the code gdn_prefill would return.
+ */
+int gdn_prefill_validate(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, void *h_state, int h_state_is_table, void *out,
+                         void *scratch, size_t scratch_bytes, int B, int T, int nk, int nv,
+                         int dk, int dv, const gdn_strides *strides, const gdn_varlen *varlen);
+
+/*
+ * The prefill forward.
+ *   q, k, v     bf16 device pointers (see Conventions for addressing).
+ *   g, beta     float device pointers.
+ *   h_state     float state, read as the initial state and OVERWRITTEN with
+ *               the final state.  h_state_is_table == 0: contiguous
+ *               [B][nv][dk][dv].  == 1: a device array of B device pointers,
+ *               entry i -> [nv][dk][dv] of sequence i (the page's pointer
+ *               table, one state per request).
+ *   out         bf16 [N_tok][nv][dv].
+ *   scratch     device buffer of >= gdn_prefill_scratch_bytes(...) bytes; on
+ *               return it holds the intermediates in the documented layout
+ *               (the entry states in region s_entry).
+ *   B, T        dense: B sequences of T tokens.  Ragged: B sequences, T is the
+ *               total token count cu_seqlens[B] (used for validation only);
+ *               with T == 0 the token pointers (q, k, v, g, beta, out) may be
+ *               NULL.
+ *   stream      hipStream_t.
+ * A ragged sequence of length 0 leaves its state unchanged and writes nothing.
+ */
+int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                void *h_state, int h_state_is_table, void *out, void *scratch,
+                size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
+                const gdn_strides *strides, const gdn_varlen *varlen, void *stream);
+
+/*
+ * One stage of gdn_prefill (1, 2 or 3), same arguments, same validation.
+ * Stage s reads what stage s-1 left in scratch; running 1, 2, 3 in order on
+ * one stream is exactly gdn_prefill.  For callers that time or interleave the
+ * stages.
+ */
+int gdn_prefill_stage(int stage, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, void *h_state, int h_state_is_table, void *out,
+                      void *scratch, size_t scratch_bytes, int B, int T, int nk, int nv, int dk,
+                      int dv, const gdn_strides *strides, const gdn_varlen *varlen,
+                      void *stream);
+
+/*
+ * Host-side check of ragged offsets already copied to host memory:
+ * cu_seqlens non-decreasing from 0, cu_chunks[i+1]-cu_chunks[i] =
+ * ceil(len_i/64), max_chunks and total_chunks consistent.  gdn_prefill cannot
+ * read device offsets without synchronising, so it trusts them; callers that
+ * build offsets at run time can check them here first.  The kernels still
+ * skip any slot that would fall outside total_chunks.
+ */
+int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *cu_chunks_host,
+                          int32_t max_chunks, int32_t total_chunks);
+
+/* Text of the last error on the calling thread ("" after success). */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_PREFILL_H */

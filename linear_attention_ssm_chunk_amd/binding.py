@@ -1,0 +1,165 @@
+"""ctypes binding of libgdn_prefill.so (include/gdn_prefill.h).
+
+Argument marshalling only: every function here converts its arguments to C
+types and calls the function of the same name in the library.  Pointer
+arguments take an int (a device address) or any object with ``data_ptr()``
+(a torch tensor).  The library must have been built
+(``python -m linear_attention_ssm_chunk_amd.build``); if it is missing, loading
+fails with an error -- there is no other code path.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn_prefill.so")
+
+GDN_OK = 0
+GDN_EINVAL = -1
+GDN_EUNSUPPORTED = -2
+GDN_ESCRATCH = -3
+GDN_EHIP = -4
+GDN_CHUNK = 64
+GDN_HEAD_DIM = 128
+
+
+class gdn_strides(ctypes.Structure):
+    _fields_ = [("qk_row", ctypes.c_int64), ("v_row", ctypes.c_int64), ("gb_row", ctypes.c_int64)]
+
+
+class gdn_varlen(ctypes.Structure):
+    _fields_ = [("cu_seqlens", ctypes.c_void_p), ("cu_chunks", ctypes.c_void_p),
+                ("max_chunks", ctypes.c_int32), ("total_chunks", ctypes.c_int32)]
+
+
+class gdn_scratch_layout(ctypes.Structure):
+    _fields_ = [("gc", ctypes.c_size_t), ("w", ctypes.c_size_t), ("u", ctypes.c_size_t),
+                ("s_entry", ctypes.c_size_t), ("uc", ctypes.c_size_t), ("total", ctypes.c_size_t),
+                ("slots", ctypes.c_int64)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"gdn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m linear_attention_ssm_chunk_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        common = [vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, i32, i32, i32, i32, i32, i32,
+                  ctypes.POINTER(gdn_strides), ctypes.POINTER(gdn_varlen)]
+        L.gdn_prefill.argtypes = common + [vp]
+        L.gdn_prefill.restype = i32
+        L.gdn_prefill_stage.argtypes = [i32] + common + [vp]
+        L.gdn_prefill_stage.restype = i32
+        L.gdn_prefill_validate.argtypes = common
+        L.gdn_prefill_validate.restype = i32
+        L.gdn_prefill_scratch_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen)]
+        L.gdn_prefill_scratch_bytes.restype = sz
+        L.gdn_prefill_scratch_layout.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen),
+                                                 ctypes.POINTER(gdn_scratch_layout)]
+        L.gdn_prefill_scratch_layout.restype = i32
+        L.gdn_varlen_check_host.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.c_int32, ctypes.c_int32]
+        L.gdn_varlen_check_host.restype = i32
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _strides(s):
+    if s is None or isinstance(s, gdn_strides):
+        return s
+    return gdn_strides(*s)
+
+
+def _varlen(v):
+    if v is None or isinstance(v, gdn_varlen):
+        return v
+    cu_s, cu_c, mx, tot = v
+    return gdn_varlen(_ptr(cu_s), _ptr(cu_c), int(mx), int(tot))
+
+
+def _ref(struct):
+    return ctypes.byref(struct) if struct is not None else None
+
+
+def gdn_last_error():
+    return lib().gdn_last_error().decode()
+
+
+def _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+            B, T, nk, nv, dk, dv, strides, varlen):
+    st, vl = _strides(strides), _varlen(varlen)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h_state), int(h_state_is_table),
+            _ptr(out), _ptr(scratch), int(scratch_bytes), B, T, nk, nv, dk, dv, _ref(st), _ref(vl))
+    return args, (st, vl)
+
+
+def gdn_prefill(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                B, T, nk, nv, dk, dv, strides, varlen, stream):
+    """Enqueue the prefill on ``stream`` (a hipStream_t as int).  Raises
+    GdnError on a nonzero return."""
+    args, keep = _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen)
+    rc = lib().gdn_prefill(*args, ctypes.c_void_p(int(stream)))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return rc
+
+
+def gdn_prefill_stage(stage, q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                      B, T, nk, nv, dk, dv, strides, varlen, stream):
+    args, keep = _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen)
+    rc = lib().gdn_prefill_stage(int(stage), *args, ctypes.c_void_p(int(stream)))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return rc
+
+
+def gdn_prefill_validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen):
+    """Return code of the pure host validation (no exception)."""
+    args, keep = _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen)
+    return lib().gdn_prefill_validate(*args)
+
+
+def gdn_prefill_scratch_bytes(B, T, nv, dk, dv, varlen=None):
+    vl = _varlen(varlen)
+    return lib().gdn_prefill_scratch_bytes(B, T, nv, dk, dv, _ref(vl))
+
+
+def gdn_prefill_scratch_layout(B, T, nv, dk, dv, varlen=None):
+    vl = _varlen(varlen)
+    out = gdn_scratch_layout()
+    rc = lib().gdn_prefill_scratch_layout(B, T, nv, dk, dv, _ref(vl), ctypes.byref(out))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return out
+
+
+def gdn_varlen_check_host(B, cu_seqlens, cu_chunks, max_chunks, total_chunks):
+    """Check host copies of the ragged offsets (sequences of ints)."""
+    a = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+    b = (ctypes.c_int32 * len(cu_chunks))(*[int(x) for x in cu_chunks])
+    return lib().gdn_varlen_check_host(B, a, b, int(max_chunks), int(total_chunks))

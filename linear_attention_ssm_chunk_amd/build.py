@@ -1,0 +1,52 @@
+"""Build libgdn_prefill.so in-tree with hipcc for gfx950.
+
+    python -m linear_attention_ssm_chunk_amd.build
+
+Every HIP source is compiled with packed FP32 math disabled
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns
+that it does not know the feature, which is harmless.
+"""
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libgdn_prefill.so")
+SOURCES = ["gdn_api.hip", "k1_chunk_cumsum_recompute_wu.hip", "k2_chunk_delta_h.hip", "k3_chunk_fwd_o.hip"]
+ARCH = "gfx950"
+
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose=False):
+    """Compile every kernel and the C ABI into one shared library."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc()] + FLAGS + srcs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if err.strip() and verbose:
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,277 @@
+// gdn_api.hip -- the C ABI of include/gdn_prefill.h: argument validation
+// (pure host logic), the scratch layout, and the three launches on the
+// caller's stream.
+//
+// Convention from the page "spark_model/layers/ops/ssm_gdn_a3.rs"
+// (gdn_tc_spine_reject): every rejection names the guard that rejected, and a
+// path that cannot run fails loudly; nothing here falls back to anything.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gdn_prefill.h"
+#include "gdn_params.h"
+
+namespace gdn {
+hipError_t launch_stage1(const Params &p, hipStream_t stream);
+hipError_t launch_stage2(const Params &p, hipStream_t stream);
+hipError_t launch_stage3(const Params &p, hipStream_t stream);
+} // namespace gdn
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return GDN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void *ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// Chunk slots per head, or -1 when the sizes are invalid.
+int64_t chunk_slots(int B, int T, const gdn_varlen *varlen) {
+  if (B <= 0) return -1;
+  if (varlen) {
+    if (varlen->total_chunks < 0 || varlen->max_chunks < 0) return -1;
+    return varlen->total_chunks;
+  }
+  if (T <= 0) return -1;
+  return int64_t(B) * ((int64_t(T) + GDN_CHUNK - 1) / GDN_CHUNK);
+}
+
+int layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen, gdn_scratch_layout *out) {
+  if (dk != GDN_HEAD_DIM || dv != GDN_HEAD_DIM)
+    return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
+  if (nv <= 0) return fail(GDN_EINVAL, "nv=%d must be positive", nv);
+  const int64_t chunks = chunk_slots(B, T, varlen);
+  if (chunks < 0)
+    return fail(GDN_EINVAL, "sizes: B=%d T=%d%s give no valid chunk count", B, T,
+                varlen ? " (ragged: max_chunks/total_chunks must be >= 0)" : "");
+  const int64_t slots = chunks * nv;
+  size_t off = 0;
+  out->slots = slots;
+  out->gc = off;
+  off = align256(off + size_t(slots) * gdn::kGcBytes);
+  out->w = off;
+  off = align256(off + size_t(slots) * gdn::kWBytes);
+  out->u = off;
+  off = align256(off + size_t(slots) * gdn::kUBytes);
+  out->s_entry = off;
+  off = align256(off + size_t(slots) * gdn::kSBytes);
+  out->uc = off;
+  off = align256(off + size_t(slots) * gdn::kUcBytes);
+  out->total = off > 256 ? off : 256; // never 0 for a valid problem
+  return ok();
+}
+
+int validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
+             void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
+             int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+             const gdn_varlen *varlen, gdn_scratch_layout *lay) {
+  if (dk != GDN_HEAD_DIM || dv != GDN_HEAD_DIM)
+    return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
+  if (nk <= 0 || nv <= 0) return fail(GDN_EINVAL, "head counts: nk=%d nv=%d must be positive", nk, nv);
+  if (nv % nk != 0) return fail(GDN_EINVAL, "GQA grouping: nv=%d is not a multiple of nk=%d", nv, nk);
+  if (nv > 65535) return fail(GDN_EINVAL, "nv=%d exceeds the grid's y extent (65535)", nv);
+  if (B <= 0 || B > 65535) return fail(GDN_EINVAL, "B=%d must be in 1..65535", B);
+  if (varlen == nullptr && T <= 0) return fail(GDN_EINVAL, "T=%d must be positive for dense input", T);
+  if (varlen != nullptr && T < 0) return fail(GDN_EINVAL, "T=%d (total tokens) must be >= 0", T);
+  // a ragged call with no tokens reads and writes no token rows
+  const bool no_tokens = (varlen != nullptr && T == 0);
+  if (!no_tokens && (!q || !k || !v)) return fail(GDN_EINVAL, "null pointer: q, k and v are required");
+  if (!no_tokens && (!g || !beta)) return fail(GDN_EINVAL, "null pointer: g and beta are required");
+  if (!h_state) return fail(GDN_EINVAL, "null pointer: h_state is required");
+  if (!no_tokens && !out) return fail(GDN_EINVAL, "null pointer: out is required");
+  if (!scratch) return fail(GDN_EINVAL, "null pointer: scratch is required");
+  if (!strides) return fail(GDN_EINVAL, "null pointer: strides is required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(GDN_EINVAL, "alignment: q, k and v must be 16-byte aligned (16-byte vector loads)");
+  if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_EINVAL, "alignment: g and beta must be 4-byte aligned");
+  if (!aligned(h_state, h_state_is_table ? 8 : 16))
+    return fail(GDN_EINVAL, "alignment: h_state must be 16-byte aligned (8 for a pointer table)");
+  if (!aligned(out, 16)) return fail(GDN_EINVAL, "alignment: out must be 16-byte aligned");
+  if (!aligned(scratch, 256)) return fail(GDN_EINVAL, "alignment: scratch must be 256-byte aligned");
+  if (h_state_is_table != 0 && h_state_is_table != 1)
+    return fail(GDN_EINVAL, "h_state_is_table=%d must be 0 or 1", h_state_is_table);
+  if (strides->qk_row % 8 != 0 || strides->v_row % 8 != 0)
+    return fail(GDN_EINVAL,
+                "strides: qk_row=%lld and v_row=%lld must be multiples of 8 (rows are read 16 bytes at a time)",
+                (long long)strides->qk_row, (long long)strides->v_row);
+  if (strides->qk_row < int64_t(nk) * GDN_HEAD_DIM)
+    return fail(GDN_EINVAL, "strides: qk_row=%lld is smaller than nk*128=%d", (long long)strides->qk_row,
+                nk * GDN_HEAD_DIM);
+  if (strides->v_row < int64_t(nv) * GDN_HEAD_DIM)
+    return fail(GDN_EINVAL, "strides: v_row=%lld is smaller than nv*128=%d", (long long)strides->v_row,
+                nv * GDN_HEAD_DIM);
+  if (strides->gb_row < nv)
+    return fail(GDN_EINVAL, "strides: gb_row=%lld is smaller than nv=%d", (long long)strides->gb_row, nv);
+  if (varlen) {
+    if (!varlen->cu_seqlens || !varlen->cu_chunks)
+      return fail(GDN_EINVAL, "ragged: cu_seqlens and cu_chunks are required");
+    if (!aligned(varlen->cu_seqlens, 4) || !aligned(varlen->cu_chunks, 4))
+      return fail(GDN_EINVAL, "ragged: cu_seqlens and cu_chunks must be 4-byte aligned");
+    if (varlen->max_chunks < 0 || varlen->total_chunks < 0)
+      return fail(GDN_EINVAL, "ragged: max_chunks=%d and total_chunks=%d must be >= 0", varlen->max_chunks,
+                  varlen->total_chunks);
+    if (varlen->max_chunks > varlen->total_chunks)
+      return fail(GDN_EINVAL, "ragged: max_chunks=%d exceeds total_chunks=%d", varlen->max_chunks,
+                  varlen->total_chunks);
+    if (int64_t(varlen->total_chunks) * GDN_CHUNK < int64_t(T))
+      return fail(GDN_EINVAL, "ragged: total_chunks=%d cannot hold T=%d tokens", varlen->total_chunks, T);
+  }
+  int rc = layout(B, T, nv, dk, dv, varlen, lay);
+  if (rc != GDN_OK) return rc;
+  if (scratch_bytes < lay->total)
+    return fail(GDN_ESCRATCH, "scratch: %zu bytes given, %zu needed", scratch_bytes, lay->total);
+  return ok();
+}
+
+gdn::Params make_params(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        void *h_state, int h_state_is_table, void *out, void *scratch, int B, int T,
+                        int nk, int nv, const gdn_strides *strides, const gdn_varlen *varlen,
+                        const gdn_scratch_layout &lay) {
+  gdn::Params p{};
+  unsigned char *base = static_cast<unsigned char *>(scratch);
+  p.q = static_cast<const uint16_t *>(q);
+  p.k = static_cast<const uint16_t *>(k);
+  p.v = static_cast<const uint16_t *>(v);
+  p.g = g;
+  p.beta = beta;
+  p.h_state = h_state;
+  p.h_is_table = h_state_is_table;
+  p.out = static_cast<uint16_t *>(out);
+  p.gc = reinterpret_cast<float *>(base + lay.gc);
+  p.w = reinterpret_cast<float *>(base + lay.w);
+  p.u = reinterpret_cast<float *>(base + lay.u);
+  p.s_entry = reinterpret_cast<uint16_t *>(base + lay.s_entry);
+  p.uc = reinterpret_cast<uint16_t *>(base + lay.uc);
+  p.qk_row = strides->qk_row;
+  p.v_row = strides->v_row;
+  p.gb_row = strides->gb_row;
+  p.B = B;
+  p.T = T;
+  p.nk = nk;
+  p.nv = nv;
+  if (varlen) {
+    p.n_chunks = 0;
+    p.max_chunks = varlen->max_chunks;
+    p.total_chunks = varlen->total_chunks;
+    p.cu_seqlens = varlen->cu_seqlens;
+    p.cu_chunks = varlen->cu_chunks;
+  } else {
+    p.n_chunks = (T + GDN_CHUNK - 1) / GDN_CHUNK;
+    p.max_chunks = p.n_chunks;
+    p.total_chunks = B * p.n_chunks;
+    p.cu_seqlens = nullptr;
+    p.cu_chunks = nullptr;
+  }
+  return p;
+}
+
+int run_stage(int stage, const gdn::Params &p, hipStream_t stream) {
+  static const char *names[4] = {"", "chunk_cumsum_recompute_wu", "chunk_delta_h", "chunk_fwd_o"};
+  if (p.max_chunks == 0) return ok(); // every sequence is empty: nothing to do
+  hipError_t e = hipSuccess;
+  if (stage == 1) e = gdn::launch_stage1(p, stream);
+  else if (stage == 2) e = gdn::launch_stage2(p, stream);
+  else e = gdn::launch_stage3(p, stream);
+  if (e != hipSuccess)
+    return fail(GDN_EHIP, "launch of %s failed: %s", names[stage], hipGetErrorString(e));
+  return ok();
+}
+
+} // namespace
+
+extern "C" {
+
+size_t gdn_prefill_scratch_bytes(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen) {
+  gdn_scratch_layout lay;
+  if (layout(B, T, nv, dk, dv, varlen, &lay) != GDN_OK) return 0;
+  return lay.total;
+}
+
+int gdn_prefill_scratch_layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen,
+                               gdn_scratch_layout *out) {
+  if (!out) return fail(GDN_EINVAL, "null pointer: layout output is required");
+  return layout(B, T, nv, dk, dv, varlen, out);
+}
+
+int gdn_prefill_validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         void *h_state, int h_state_is_table, void *out, void *scratch,
+                         size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
+                         const gdn_strides *strides, const gdn_varlen *varlen) {
+  gdn_scratch_layout lay;
+  return validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk, nv,
+                  dk, dv, strides, varlen, &lay);
+}
+
+int gdn_prefill_stage(int stage, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, void *h_state, int h_state_is_table, void *out, void *scratch,
+                      size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
+                      const gdn_strides *strides, const gdn_varlen *varlen, void *stream) {
+  if (stage < 1 || stage > 3) return fail(GDN_EINVAL, "stage=%d must be 1, 2 or 3", stage);
+  gdn_scratch_layout lay;
+  int rc = validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk,
+                    nv, dk, dv, strides, varlen, &lay);
+  if (rc != GDN_OK) return rc;
+  const gdn::Params p = make_params(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, B, T, nk,
+                                    nv, strides, varlen, lay);
+  return run_stage(stage, p, static_cast<hipStream_t>(stream));
+}
+
+int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
+                int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+                const gdn_varlen *varlen, void *stream) {
+  gdn_scratch_layout lay;
+  int rc = validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk,
+                    nv, dk, dv, strides, varlen, &lay);
+  if (rc != GDN_OK) return rc;
+  const gdn::Params p = make_params(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, B, T, nk,
+                                    nv, strides, varlen, lay);
+  for (int stage = 1; stage <= 3; ++stage) {
+    rc = run_stage(stage, p, static_cast<hipStream_t>(stream));
+    if (rc != GDN_OK) return rc;
+  }
+  return GDN_OK;
+}
+
+int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *cu_chunks_host,
+                          int32_t max_chunks, int32_t total_chunks) {
+  if (B <= 0) return fail(GDN_EINVAL, "B=%d must be positive", B);
+  if (!cu_seqlens_host || !cu_chunks_host) return fail(GDN_EINVAL, "null pointer: offsets are required");
+  if (cu_seqlens_host[0] != 0 || cu_chunks_host[0] != 0)
+    return fail(GDN_EINVAL, "ragged: cu_seqlens[0] and cu_chunks[0] must be 0");
+  int32_t mx = 0;
+  for (int i = 0; i < B; ++i) {
+    const int64_t len = int64_t(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
+    const int64_t nch = int64_t(cu_chunks_host[i + 1]) - cu_chunks_host[i];
+    if (len < 0) return fail(GDN_EINVAL, "ragged: cu_seqlens decreases at sequence %d", i);
+    if (nch != (len + GDN_CHUNK - 1) / GDN_CHUNK)
+      return fail(GDN_EINVAL, "ragged: sequence %d has %lld tokens but %lld chunks (needs ceil(len/64))", i,
+                  (long long)len, (long long)nch);
+    if (nch > mx) mx = int32_t(nch);
+  }
+  if (mx != max_chunks)
+    return fail(GDN_EINVAL, "ragged: max_chunks=%d but the longest sequence has %d chunks", max_chunks, mx);
+  if (cu_chunks_host[B] != total_chunks)
+    return fail(GDN_EINVAL, "ragged: total_chunks=%d but cu_chunks[B]=%d", total_chunks, cu_chunks_host[B]);
+  return ok();
+}
+
+const char *gdn_last_error(void) { return g_err; }
+
+} // extern "C"

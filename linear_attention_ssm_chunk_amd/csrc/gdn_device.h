@@ -1,0 +1,163 @@
+// gdn_device.h -- device helpers for the gfx950 kernels: MFMA fragments,
+// bf16 conversion and the sequence / slot bookkeeping shared by all stages.
+//
+// MFMA fragment conventions (v_mfma_f32_16x16x32_bf16, wave64; lane l,
+// r = l % 16, q = l / 16):
+//   A (16 x 32): lane holds row r, eight k values
+//   B (32 x 16): lane holds column r, eight k values
+//   C (16 x 16): lane holds column r, rows 4q .. 4q+3
+// The k order inside a lane is free as long as A and B use the same one.  Two
+// orders are used:
+//   contiguous  element e <-> k = 8q + e             (operands read from memory)
+//   chain       element e <-> k = 4q + e      (e < 4)
+//                             k = 16 + 4q + e - 4 (e >= 4)
+// The chain order makes the C fragments of two vertically stacked 16x16
+// tiles an operand of the next product without moving data between lanes:
+// registers (tile 2j, tile 2j+1) of a C result are exactly the k = 32j..32j+31
+// block of a B (or, read as its transpose, an A) operand.
+// A product with an identity operand moves a tile between the two
+// orientations in registers (exact for bf16 data): that is how these kernels
+// transpose, instead of staging through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_params.h"
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 zero8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, to_bf16(x));
+}
+
+// Pack four floats (consecutive elements of one lane) as 4 bf16 = 8 bytes.
+__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
+  return u32x2{f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
+               f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16)};
+}
+
+// Chain-order fragment from two C tiles (tile for k 0..15 and k 16..31).
+__device__ __forceinline__ bf16x8 chain_frag(const f32x4 &lo_tile, const f32x4 &hi_tile) {
+  bf16x8 f;
+  f[0] = to_bf16(lo_tile[0]); f[1] = to_bf16(lo_tile[1]);
+  f[2] = to_bf16(lo_tile[2]); f[3] = to_bf16(lo_tile[3]);
+  f[4] = to_bf16(hi_tile[0]); f[5] = to_bf16(hi_tile[1]);
+  f[6] = to_bf16(hi_tile[2]); f[7] = to_bf16(hi_tile[3]);
+  return f;
+}
+
+// Split eight floats into hi = bf16(x) and lo = bf16(x - hi): hi + lo carries
+// about 16 mantissa bits, so a product of two split operands done as
+// hi*hi + hi*lo + lo*hi keeps ~2^-17 relative error with bf16 MFMA.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h = to_bf16(x[e]);
+    hi[e] = h;
+    lo[e] = to_bf16(x[e] - (float)h);
+  }
+}
+
+// Chain-order split fragment from two C tiles.
+__device__ __forceinline__ void chain_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi,
+                                            bf16x8 &lo) {
+  float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  split8(x, hi, lo);
+}
+
+// Identity operands.  B-side identity selecting k = 16*half + column under the
+// contiguous k order, and under the chain k order.
+__device__ __forceinline__ bf16x8 ident_contig(int lane, int half) {
+  const int q = lane >> 4, r = lane & 15;
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = to_bf16((8 * q + e == 16 * half + r) ? 1.f : 0.f);
+  return f;
+}
+__device__ __forceinline__ bf16x8 ident_chain(int lane, int half) {
+  const int q = lane >> 4, r = lane & 15;
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int kk = (e < 4) ? 4 * q + e : 16 + 4 * q + (e - 4);
+    f[e] = to_bf16((kk == 16 * half + r) ? 1.f : 0.f);
+  }
+  return f;
+}
+
+__device__ __forceinline__ bf16x8 load16_bf16x8(const uint16_t *p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 load8(const uint16_t *p) {
+  return *reinterpret_cast<const u32x2 *>(p);
+}
+__device__ __forceinline__ bf16x8 join8(const u32x2 &a, const u32x2 &b) {
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// Where a sequence lives.  Ragged offsets are checked here so that a bad table
+// skips the sequence instead of writing outside the scratch.
+struct Seq {
+  int64_t tok0;   // first token row
+  int len;        // tokens
+  int64_t chunk0; // first chunk slot (per head)
+  int nchunks;
+  bool ok;
+};
+
+__device__ __forceinline__ Seq seq_of(const Params &p, int i) {
+  Seq s;
+  if (p.cu_seqlens == nullptr) {
+    s.tok0 = int64_t(i) * p.T;
+    s.len = p.T;
+    s.chunk0 = int64_t(i) * p.n_chunks;
+    s.nchunks = p.n_chunks;
+    s.ok = true;
+  } else {
+    const int a = p.cu_seqlens[i], b = p.cu_seqlens[i + 1];
+    const int ca = p.cu_chunks[i], cb = p.cu_chunks[i + 1];
+    s.tok0 = a;
+    s.len = b - a;
+    s.chunk0 = ca;
+    s.nchunks = cb - ca;
+    s.ok = (a >= 0) && (s.len >= 0) && (ca >= 0) && (cb <= p.total_chunks) &&
+           (s.nchunks == (s.len + kChunk - 1) / kChunk) && (s.nchunks <= p.max_chunks);
+  }
+  return s;
+}
+
+// Chunk slot of (sequence s, v-head h, chunk c): [seq][head][chunk] order.
+__device__ __forceinline__ int64_t slot_of(const Params &p, const Seq &s, int h, int c) {
+  return s.chunk0 * p.nv + int64_t(h) * s.nchunks + c;
+}
+
+__device__ __forceinline__ float *state_of(const Params &p, int i, int h) {
+  if (p.h_is_table) {
+    float *base = reinterpret_cast<float *const *>(p.h_state)[i];
+    return base + int64_t(h) * kDim * kDim;
+  }
+  return reinterpret_cast<float *>(p.h_state) + (int64_t(i) * p.nv + h) * kDim * kDim;
+}
+
+} // namespace gdn

@@ -1,0 +1,40 @@
+// gdn_params.h -- one parameter block shared by the host launcher and the three
+// kernels, so the two sides cannot disagree about sizes or layouts (the page
+// "spark_model/layers/ops/ssm_gdn_a3.rs" makes the same point about its
+// shared-memory footprint constant GDN_TC_SMEM).
+#pragma once
+
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;    // tokens per chunk
+constexpr int kDim = 128;     // dk = dv
+constexpr int kThreads = 256; // every kernel: 4 waves of 64
+
+// Bytes per chunk slot of each scratch region (see include/gdn_prefill.h).
+constexpr int64_t kGcBytes = int64_t(kChunk) * 4;
+constexpr int64_t kWBytes = int64_t(kChunk) * kDim * 4;
+constexpr int64_t kUBytes = int64_t(kChunk) * kDim * 4;
+constexpr int64_t kSBytes = int64_t(kDim) * kDim * 2;
+constexpr int64_t kUcBytes = int64_t(kDim) * kChunk * 2;
+
+struct Params {
+  // inputs (bf16 as raw 16-bit patterns)
+  const uint16_t *q, *k, *v;
+  const float *g, *beta;
+  // state: contiguous [B][nv][dk][dv] or a device table of B pointers
+  void *h_state;
+  int h_is_table;
+  uint16_t *out; // bf16 [N_tok][nv][dv]
+  // scratch regions
+  float *gc, *w, *u;
+  uint16_t *s_entry, *uc;
+  int64_t qk_row, v_row, gb_row; // token-row pitches in elements
+  int B, T, nk, nv;
+  int n_chunks;                  // dense: ceil(T/64)
+  int max_chunks, total_chunks;  // grid extent, chunk slots per head
+  const int32_t *cu_seqlens, *cu_chunks; // NULL = dense
+};
+
+} // namespace gdn

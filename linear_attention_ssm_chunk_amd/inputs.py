@@ -6,8 +6,11 @@ module that both the oracle side (tests, bench cpu_baseline) and the GPU side
 use, and it imports neither.
 
 Recipe (fixed, documented in the design notes):
-  * ``numpy.random.default_rng(seed)``; draw order: sequence lengths (ragged
-    workload only), q, k, v, g, beta, h0.
+  * ragged workload: sequence lengths from ``numpy.random.default_rng(seed)``;
+  * ``numpy.random.SeedSequence(seed).spawn(6)``: one stream per array, in the
+    order q, k, v, g, beta, h0; per-token arrays are drawn in blocks of 4096
+    tokens, block b from the b-th child of the array's stream (so blocks can
+    be drawn in parallel and the result does not depend on thread count).
   * q, k ~ N(0, 1) float32, L2-normalised per (token, head) 128-vector in
     float32, then rounded to bf16 (round-to-nearest-even); v ~ N(0, 1) -> bf16.
   * g = -softplus(N(0, 1)) float32 (via logaddexp); beta = sigmoid(N(0, 1))
@@ -105,15 +108,22 @@ class Problem:
         n = [-(-L // CHUNK) for L in self.lengths]
         return np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
 
-    def seq(self, i, heads=None):
-        """float64 arrays of sequence ``i`` for the oracle; ``heads`` selects
-        v-heads (and keeps every k-head so the grouping is unchanged)."""
-        a, b = int(self.cu_seqlens[i]), int(self.cu_seqlens[i + 1])
-        hs = slice(None) if heads is None else list(heads)
-        return dict(q=bf16_to_f64(self.q[a:b]), k=bf16_to_f64(self.k[a:b]),
-                    v=bf16_to_f64(self.v[a:b][:, hs]), g=self.g[a:b][:, hs].astype(np.float64),
-                    beta=self.beta[a:b][:, hs].astype(np.float64),
-                    h0=self.h0[i][hs].astype(np.float64))
+
+BLOCK = 4096  # tokens per independent random stream
+
+
+def _blocks(N):
+    return [(a, min(N, a + BLOCK)) for a in range(0, N, BLOCK)] or [(0, 0)]
+
+
+def _fill(seed_seq, N, fn, pool):
+    """Concatenate fn(rng, rows) over token blocks, block b drawn from the
+    b-th child of ``seed_seq`` (so the result does not depend on threads)."""
+    blocks = _blocks(N)
+    kids = seed_seq.spawn(len(blocks))
+    parts = list(pool.map(lambda ab: fn(np.random.default_rng(kids[ab[0]]), ab[1][1] - ab[1][0]),
+                          enumerate(blocks)))
+    return np.concatenate(parts, axis=0)
 
 
 def _unit_rows_bf16(rng, shape):
@@ -122,18 +132,29 @@ def _unit_rows_bf16(rng, shape):
     return f32_to_bf16_bits(x)
 
 
-def make_problem(lengths, nk, nv, seed, h0="normal", rng=None):
-    """Draw q, k, v, g, beta, h0 for the given sequence lengths."""
-    rng = np.random.default_rng(seed) if rng is None else rng
+def make_problem(lengths, nk, nv, seed, h0="normal"):
+    """Draw q, k, v, g, beta, h0 for the given sequence lengths.
+
+    ``SeedSequence(seed).spawn(6)`` gives one stream per array in the order q,
+    k, v, g, beta, h0; the per-token arrays are drawn in blocks of 4096 tokens,
+    block b from child b of the array's stream."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
     N = int(sum(lengths))
-    q = _unit_rows_bf16(rng, (N, nk, HEAD_DIM))
-    k = _unit_rows_bf16(rng, (N, nk, HEAD_DIM))
-    v = f32_to_bf16_bits(rng.standard_normal((N, nv, HEAD_DIM), dtype=np.float32))
-    g = (-np.logaddexp(np.float32(0), rng.standard_normal((N, nv), dtype=np.float32))).astype(np.float32)
-    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((N, nv), dtype=np.float32)))).astype(np.float32)
+    ss = np.random.SeedSequence(seed).spawn(6)
+    with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as pool:
+        q = _fill(ss[0], N, lambda r, n: _unit_rows_bf16(r, (n, nk, HEAD_DIM)), pool)
+        k = _fill(ss[1], N, lambda r, n: _unit_rows_bf16(r, (n, nk, HEAD_DIM)), pool)
+        v = _fill(ss[2], N, lambda r, n: f32_to_bf16_bits(r.standard_normal((n, nv, HEAD_DIM), dtype=np.float32)),
+                  pool)
+        g = _fill(ss[3], N, lambda r, n: (-np.logaddexp(np.float32(0), r.standard_normal((n, nv), dtype=np.float32))
+                                          ).astype(np.float32), pool)
+        beta = _fill(ss[4], N, lambda r, n: (1.0 / (1.0 + np.exp(-r.standard_normal((n, nv), dtype=np.float32)))
+                                             ).astype(np.float32), pool)
     nseq = len(lengths)
     if h0 == "normal":
-        h = (0.02 * rng.standard_normal((nseq, nv, HEAD_DIM, HEAD_DIM), dtype=np.float32)).astype(np.float32)
+        h = (0.02 * np.random.default_rng(ss[5]).standard_normal((nseq, nv, HEAD_DIM, HEAD_DIM),
+                                                                 dtype=np.float32)).astype(np.float32)
     else:
         h = np.zeros((nseq, nv, HEAD_DIM, HEAD_DIM), dtype=np.float32)
     return Problem(list(lengths), nk, nv, q, k, v, g, beta, h, seed)
@@ -146,9 +167,7 @@ def make_workload(index, seed=None):
     seed = index if seed is None else seed
     if "nseq" in w:
         lengths, used = ragged_lengths(seed, w["nseq"])
-        rng = np.random.default_rng(used)
-        rng.integers(1, 16384 + 1, size=w["nseq"])  # consume the length draw
-        p = make_problem(lengths, w["nk"], w["nv"], used, w["h0"], rng=rng)
+        p = make_problem(lengths, w["nk"], w["nv"], used, w["h0"])
         p.meta["length_seed"] = used
     else:
         p = make_problem([w["T"]] * w["B"], w["nk"], w["nv"], seed, w["h0"])

@@ -1,0 +1,146 @@
+"""The C ABI on the host (CPU only): the library loads, exports every function
+include/gdn_prefill.h declares, and rejects every malformed call by name
+before touching the GPU."""
+
+import os
+import re
+
+import pytest
+
+from linear_attention_ssm_chunk_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_prefill.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(B.LIB_PATH):
+        from linear_attention_ssm_chunk_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(gdn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"gdn_prefill", "gdn_prefill_stage", "gdn_prefill_validate", "gdn_prefill_scratch_bytes",
+            "gdn_prefill_scratch_layout", "gdn_varlen_check_host", "gdn_last_error"} <= set(names)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+# fake, well-aligned device addresses: validation never dereferences them
+P = 0x7F0000000000
+
+
+def good_args(**over):
+    a = dict(q=P, k=P + 4096, v=P + 8192, g=P + 16384, beta=P + 16384 + 128, h_state=P + 2 ** 30,
+             h_state_is_table=0, out=P + 2 ** 31, scratch=P + 2 ** 32, scratch_bytes=None,
+             B=2, T=200, nk=2, nv=4, dk=128, dv=128, strides=(2 * 128, 4 * 128, 4), varlen=None)
+    a.update(over)
+    if a["scratch_bytes"] is None:
+        a["scratch_bytes"] = B.gdn_prefill_scratch_bytes(a["B"], a["T"], a["nv"], 128, 128, a["varlen"]) or 1
+    return a
+
+
+def validate(**over):
+    a = good_args(**over)
+    rc = B.gdn_prefill_validate(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h_state"], a["h_state_is_table"],
+                                a["out"], a["scratch"], a["scratch_bytes"], a["B"], a["T"], a["nk"], a["nv"],
+                                a["dk"], a["dv"], a["strides"], a["varlen"])
+    return rc, B.gdn_last_error()
+
+
+def test_good_arguments_validate():
+    rc, msg = validate()
+    assert rc == B.GDN_OK and msg == ""
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(dk=64), B.GDN_EUNSUPPORTED, "head size"),
+    (dict(dv=256), B.GDN_EUNSUPPORTED, "head size"),
+    (dict(nk=3), B.GDN_EINVAL, "GQA grouping"),
+    (dict(nk=0), B.GDN_EINVAL, "head counts"),
+    (dict(B=0), B.GDN_EINVAL, "B=0"),
+    (dict(T=0), B.GDN_EINVAL, "T=0"),
+    (dict(q=0), B.GDN_EINVAL, "null pointer"),
+    (dict(beta=0), B.GDN_EINVAL, "null pointer"),
+    (dict(h_state=0), B.GDN_EINVAL, "null pointer"),
+    (dict(out=0), B.GDN_EINVAL, "null pointer"),
+    (dict(scratch=0), B.GDN_EINVAL, "null pointer"),
+    (dict(strides=None), B.GDN_EINVAL, "strides is required"),
+    (dict(k=P + 4096 + 8), B.GDN_EINVAL, "16-byte aligned"),
+    (dict(g=P + 2), B.GDN_EINVAL, "4-byte aligned"),
+    (dict(scratch=P + 2 ** 32 + 16), B.GDN_EINVAL, "256-byte"),
+    (dict(strides=(2 * 128 + 4, 512, 4)), B.GDN_EINVAL, "multiples of 8"),
+    (dict(strides=(128, 512, 4)), B.GDN_EINVAL, "smaller than nk*128"),
+    (dict(strides=(256, 256, 4)), B.GDN_EINVAL, "smaller than nv*128"),
+    (dict(strides=(256, 512, 3)), B.GDN_EINVAL, "gb_row"),
+    (dict(h_state_is_table=2), B.GDN_EINVAL, "h_state_is_table"),
+    (dict(scratch_bytes=1024), B.GDN_ESCRATCH, "needed"),
+])
+def test_each_guard_rejects_by_name(over, code, needle):
+    rc, msg = validate(**over)
+    assert rc == code, msg
+    assert needle in msg
+
+
+def test_ragged_guards():
+    vl = B.gdn_varlen(P + 64, P + 128, 3, 5)
+    rc, msg = validate(varlen=vl, T=300, scratch_bytes=B.gdn_prefill_scratch_bytes(2, 300, 4, 128, 128, vl))
+    assert rc == B.GDN_OK, msg
+    rc, msg = validate(varlen=B.gdn_varlen(0, P + 128, 3, 5), T=300)
+    assert rc == B.GDN_EINVAL and "cu_seqlens and cu_chunks" in msg
+    rc, msg = validate(varlen=B.gdn_varlen(P + 64, P + 128, 6, 5), T=300)
+    assert rc == B.GDN_EINVAL and "max_chunks" in msg
+    rc, msg = validate(varlen=B.gdn_varlen(P + 64, P + 128, 3, 4), T=300)
+    assert rc == B.GDN_EINVAL and "cannot hold" in msg
+
+
+def test_prefill_rejects_without_touching_the_gpu():
+    a = good_args(dk=64)
+    with pytest.raises(B.GdnError) as e:
+        B.gdn_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h_state"], 0, a["out"], a["scratch"],
+                      a["scratch_bytes"], a["B"], a["T"], a["nk"], a["nv"], 64, 128, a["strides"], None, 0)
+    assert e.value.code == B.GDN_EUNSUPPORTED
+    with pytest.raises(B.GdnError) as e:
+        B.gdn_prefill_stage(4, *[good_args()[k] for k in ("q", "k", "v", "g", "beta", "h_state",
+                                                            "h_state_is_table", "out", "scratch",
+                                                            "scratch_bytes", "B", "T", "nk", "nv", "dk",
+                                                            "dv", "strides", "varlen")], 0)
+    assert "stage=4" in str(e.value)
+
+
+def test_scratch_layout_arithmetic():
+    L = B.gdn_prefill_scratch_layout(4, 8192, 32, 128, 128)
+    slots = 4 * 128 * 32
+    assert L.slots == slots and L.gc == 0
+    assert L.w == slots * 64 * 4
+    assert L.u == L.w + slots * 64 * 128 * 4
+    assert L.s_entry == L.u + slots * 64 * 128 * 4
+    assert L.uc == L.s_entry + slots * 128 * 128 * 2
+    assert L.total == L.uc + slots * 128 * 64 * 2
+    assert B.gdn_prefill_scratch_bytes(2, 0, 4, 128, 128, B.gdn_varlen(P, P, 0, 0)) == 256
+    # partial last chunk: T = 200 -> 4 chunks
+    assert B.gdn_prefill_scratch_layout(1, 200, 1, 128, 128).slots == 4
+    # ragged: total_chunks decides
+    vl = B.gdn_varlen(P, P, 2, 7)
+    assert B.gdn_prefill_scratch_layout(3, 0, 5, 128, 128, vl).slots == 35
+    assert B.gdn_prefill_scratch_bytes(1, 64, 1, 64, 128) == 0
+
+
+def test_varlen_host_check():
+    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5) == B.GDN_OK
+    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 1, 1, 4], 3, 4) == B.GDN_EINVAL
+    assert "ceil(len/64)" in B.gdn_last_error()
+    assert B.gdn_varlen_check_host(3, [0, 65, 60, 200], [0, 2, 2, 5], 3, 5) == B.GDN_EINVAL
+    assert "decreases" in B.gdn_last_error()
+    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 2, 5) == B.GDN_EINVAL
+    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 3, 6) == B.GDN_EINVAL

@@ -1,0 +1,244 @@
+"""Parity of the HIP library with the oracle, on the GPU, through the C ABI.
+
+Small problems (seconds of oracle time, several chunks and a ragged tail) are
+compared element by element, intermediates included; the full-size workloads
+run in the launch configuration bench.py times and are compared on sampled
+(sequence, head) chains, each computed by the oracle in full.  Tolerances are
+in tests/parity.py.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from linear_attention_ssm_chunk_amd import inputs as I  # noqa: E402
+from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64  # noqa: E402
+from parity import assert_within, check_problem, relfro  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_ssm_chunk_amd import binding
+    binding.lib()  # fails loudly if the library is not built
+    from linear_attention_ssm_chunk_amd.device import DeviceProblem
+    return DeviceProblem
+
+
+def run(DP, p, **kw):
+    print(f"[gpu] lengths={p.lengths[:8]}{'...' if len(p.lengths) > 8 else ''} nk={p.nk} nv={p.nv} {kw}", flush=True)
+    dp = DP(p, **kw)
+    dp.run()
+    torch.cuda.synchronize()
+    return dp
+
+
+# --------------------------------------------------------------------------
+# small problems, full comparison
+
+
+def test_workload1_tiny_full(dev):
+    p = I.make_workload(1)
+    dp = run(dev, p)
+    w = check_problem(dp, p, intermediates=True)
+    print(w)
+    assert_within(w, intermediates=True)
+
+
+@pytest.mark.parametrize("T", [200, 64, 1, 129])
+def test_dense_gqa_ragged_tail(dev, T):
+    p = I.make_problem([T, T], nk=2, nv=4, seed=100 + T)
+    dp = run(dev, p)
+    w = check_problem(dp, p, intermediates=True)
+    print(w)
+    assert_within(w, intermediates=True)
+
+
+def test_gqa_ratio3_heads_distinguishable(dev):
+    """nk=2, nv=6: each v-head must read k-head h*nk//nv (a swap fails)."""
+    p = I.make_problem([150], nk=2, nv=6, seed=7)
+    dp = run(dev, p)
+    w = check_problem(dp, p, intermediates=True)
+    assert_within(w, intermediates=True)
+
+
+def test_ragged_with_state_table(dev):
+    lens = [1, 64, 65, 130, 0, 77, 129, 3]
+    p = I.make_problem(lens, nk=1, nv=2, seed=11)
+    dp = run(dev, p, state="table", ragged=True)
+    w = check_problem(dp, p, intermediates=True)
+    print(w)
+    assert_within(w, intermediates=True)
+    # the empty sequence keeps its state bit for bit
+    assert np.array_equal(dp.state()[4], p.h0[4])
+
+
+def test_all_sequences_empty(dev):
+    p = I.make_problem([0, 0], nk=1, nv=1, seed=12)
+    dp = run(dev, p, ragged=True)
+    assert np.array_equal(dp.state(), p.h0)
+
+
+def test_packed_conv_layout_bit_identical(dev):
+    p = I.make_problem([200, 200], nk=2, nv=6, seed=13)
+    a = run(dev, p, layout="contiguous")
+    b = run(dev, p, layout="conv")
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.h, b.h)
+    assert torch.equal(a.scratch, b.scratch)
+
+
+def test_state_table_equals_contiguous(dev):
+    p = I.make_problem([100, 100, 100], nk=1, nv=2, seed=14)
+    a = run(dev, p, state="contiguous")
+    b = run(dev, p, state="table")
+    assert torch.equal(a.out, b.out)
+    assert np.array_equal(a.state(), b.state())
+
+
+def test_rerun_is_byte_identical(dev):
+    p = I.make_problem([300], nk=2, nv=4, seed=15)
+    dp = run(dev, p)
+    o1, h1 = dp.out.clone(), dp.h.clone()
+    dp.reset_state()
+    dp.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, dp.out) and torch.equal(h1, dp.h)
+
+
+def test_stages_in_order_equal_one_call(dev):
+    p = I.make_problem([190], nk=1, nv=2, seed=16)
+    a = run(dev, p)
+    b = dev(p)
+    for st in (1, 2, 3):
+        b.run_stage(st)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out) and torch.equal(a.h, b.h)
+
+
+def test_split_resume_through_in_place_state(dev):
+    """[0, T) at once equals [0, T1) then [T1, T) carried through h_state."""
+    T, T1 = 320, 130
+    p = I.make_problem([T], nk=1, nv=2, seed=17)
+    whole = run(dev, p)
+    first = I.make_problem([T1], 1, 2, seed=0)
+    second = I.make_problem([T - T1], 1, 2, seed=0)
+    for dst, sl in ((first, slice(0, T1)), (second, slice(T1, T))):
+        dst.q, dst.k, dst.v, dst.g, dst.beta = p.q[sl], p.k[sl], p.v[sl], p.g[sl], p.beta[sl]
+    first.h0 = p.h0
+    a = run(dev, first)
+    second.h0 = a.state()
+    b = run(dev, second)
+    out = np.concatenate([a.output(), b.output()])
+    assert np.abs(out - whole.output()).max() <= 2e-2
+    assert relfro(b.state().astype(np.float64), whole.state().astype(np.float64)) <= 1e-4
+
+
+# --------------------------------------------------------------------------
+# special inputs with closed-form answers
+
+
+def _one_hot_keys(rng, N, nk):
+    idx = rng.integers(0, 128, size=(N, nk))
+    k = np.zeros((N, nk, 128), np.float32)
+    np.put_along_axis(k, idx[..., None], 1.0, axis=-1)
+    return I.f32_to_bf16_bits(k)
+
+
+def test_q_equals_k_beta_one_returns_v(dev):
+    """beta = 1, q = k, exactly unit keys: o_t = v_t for any g and h0."""
+    rng = np.random.default_rng(21)
+    p = I.make_problem([200], nk=1, nv=2, seed=21)
+    p.k = _one_hot_keys(rng, 200, 1)
+    p.q = p.k.copy()
+    p.beta[:] = 1.0
+    dp = run(dev, p)
+    o = dp.output()
+    err = np.abs(o - bf16_to_f64(p.v)).max()
+    print("q=k beta=1 max err", err)
+    assert err <= 2e-2
+    assert_within(check_problem(dp, p))
+
+
+def test_beta_zero_decays_only(dev):
+    """beta = 0: o_t = exp(G_t) h0^T q_t, final state exp(sum g) h0.  The
+    decay is slowed (g * 0.01) so the final state stays inside float32 range."""
+    p = I.make_problem([150], nk=1, nv=2, seed=22)
+    p.beta[:] = 0.0
+    p.g *= np.float32(0.01)
+    dp = run(dev, p)
+    G = np.cumsum(p.g.astype(np.float64), axis=0)
+    q = bf16_to_f64(p.q)[:, 0]
+    expect = np.exp(G)[:, :, None] * np.einsum("hkd,tk->thd", p.h0[0].astype(np.float64), q)
+    assert np.abs(dp.output() - expect).max() <= 2e-2
+    hf = np.exp(G[-1])[:, None, None] * p.h0[0]
+    assert relfro(dp.state()[0].astype(np.float64), hf) <= 1e-5
+
+
+def test_one_hot_overwrite_no_decay(dev):
+    """g = 0, beta = 1, one-hot keys: each token overwrites row pi(t) of h."""
+    rng = np.random.default_rng(23)
+    p = I.make_problem([150], nk=1, nv=1, seed=23)
+    p.k = _one_hot_keys(rng, 150, 1)
+    p.g[:] = 0.0
+    p.beta[:] = 1.0
+    dp = run(dev, p)
+    h = p.h0[0, 0].astype(np.float64).copy()
+    kk = bf16_to_f64(p.k)[:, 0]
+    vv = bf16_to_f64(p.v)[:, 0]
+    for t in range(150):
+        h[np.argmax(kk[t])] = vv[t]
+    assert relfro(dp.state()[0, 0].astype(np.float64), h) <= 1e-5
+    assert_within(check_problem(dp, p))
+
+
+def test_strong_forgetting(dev):
+    p = I.make_problem([130], nk=1, nv=1, seed=24)
+    p.g[:] = -80.0
+    dp = run(dev, p)
+    assert_within(check_problem(dp, p))
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, sampled chains
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("index,samples", [
+    (2, [(0, 0), (0, 17), (0, 31)]),
+    (3, [(0, 0), (1, 9), (2, 22), (3, 31)]),
+    (4, "per_seq"),
+    (5, [(0, 0), (0, 47)]),
+])
+def test_full_workload_sampled(dev, index, samples):
+    p = I.make_workload(index)
+    kw = dict(layout="conv") if p.meta["layout"] == "conv" else {}
+    if p.meta["layout"] == "varlen_table":
+        kw = dict(state="table", ragged=True)
+    dp = run(dev, p, **kw)
+    out = dp.output()
+    assert np.all(np.isfinite(out))
+    if samples == "per_seq":
+        samples = [(i, (5 * i + 3) % p.nv) for i in range(p.nseq)]
+    worst = {}
+    for (i, h) in samples:
+        w = check_problem(dp, p, seqs=[i], heads=[h], entries=True)
+        for key, val in w.items():
+            worst[key] = max(worst.get(key, 0.0), val)
+    print(f"workload {index}: {worst}", flush=True)
+    assert_within(worst)
+
+
+def test_slow_decay_long_carry(dev):
+    """g * 0.01 keeps the state alive across many chunks, so a state that is
+    not carried (or carried wrongly) between chunks shows in every output."""
+    p = I.make_problem([700, 451], nk=2, nv=4, seed=25)
+    p.g *= np.float32(0.01)
+    dp = run(dev, p)
+    w = check_problem(dp, p, intermediates=True)
+    print(w)
+    assert_within(w, intermediates=True)
