@@ -156,7 +156,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes (three times), to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
               f"requested); run with --gpus 1", file=sys.stderr)
