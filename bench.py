@@ -40,7 +40,14 @@ KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h.hip", 
 
 
 def algorithmic(p):
-    """Per-kernel algorithmic bytes and flops for problem p (inputs.Problem)."""
+    """Per-kernel algorithmic bytes and flops for problem p (inputs.Problem).
+
+    Bytes: every operand each stage must read or write once (q, k counted once
+    per k-head).  Stage 1 reads k, g, beta and writes gc, the decays and T'
+    (16 KB per chunk-head); stage 2 reads T', k, v, the decays and the state
+    and writes the entry states (32 KB per chunk-head), uc (16 KB) and the
+    state; stage 3 reads q, k, gc, the decays, the entry states and uc and
+    writes o.  Flops: dense-tile MFMA work per chunk-head."""
     N, nk, nv = p.n_tokens, p.nk, p.nv
     slots = int(p.cu_chunks[-1]) * nv
     nseq = p.nseq
@@ -50,20 +57,21 @@ def algorithmic(p):
     v_bytes = N * nv * d * 2
     gb_bytes = N * nv * 8
     gc_bytes = slots * C * 4
-    wu_bytes = slots * C * d * 4 * 2
+    dec_bytes = slots * 2 * C * 4
+    tp_bytes = slots * C * C * 4
     s_bytes = slots * d * d * 2
     uc_bytes = slots * d * C * 2
     state_bytes = nseq * nv * d * d * 4
     o_bytes = N * nv * d * 2
     by = {
-        1: k_bytes + v_bytes + gb_bytes + gc_bytes + wu_bytes,
-        2: wu_bytes + k_bytes + gc_bytes + 2 * state_bytes + s_bytes + uc_bytes,
-        3: q_bytes + k_bytes + gc_bytes + s_bytes + uc_bytes + o_bytes,
+        1: k_bytes + gb_bytes + gc_bytes + dec_bytes + tp_bytes,
+        2: tp_bytes + k_bytes + v_bytes + dec_bytes + 2 * state_bytes + s_bytes + uc_bytes,
+        3: q_bytes + k_bytes + gc_bytes + dec_bytes // 2 + s_bytes + uc_bytes + o_bytes,
     }
-    # dense-tile flops per chunk-head: Gram 2C^2 d, WY 2C^2 (dk+dv), spine 4 C d^2,
-    # output 2 C d^2 + 2 C^2 d + 2 C^2 d
-    fl = {1: slots * (2 * C * C * d + 2 * C * C * 2 * d),
-          2: slots * (4 * C * d * d),
+    # Gram 2C^2 d; spine K h, T' R, K^T uc: 2Cd^2 + 2C^2 d + 2Cd^2; output
+    # Q S 2Cd^2, scores 2C^2 d, A uc 2C^2 d
+    fl = {1: slots * (2 * C * C * d),
+          2: slots * (4 * C * d * d + 2 * C * C * d),
           3: slots * (2 * C * d * d + 4 * C * C * d)}
     return by, fl
 

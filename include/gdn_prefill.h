@@ -11,10 +11,12 @@
  * gdn_prefill_fla:
  *   1. chunk_cumsum_recompute_wu: chunk-local cumulative log-gate gc, the
  *      strictly lower L (sharing the key Gram), and the WY/UT solves
- *      (I+L) W = beta exp(gc) K, (I+L) U = beta V;
+ *      (I+L) W = beta exp(gc) K, (I+L) U = beta V -- emitted as the UT
+ *      transform T' = (I+L)^-1 diag(beta), which gives U = T' V and
+ *      W = T' diag(exp(gc)) K;
  *   2. chunk_delta_h: a serial float32 state spine over chunks that emits each
- *      chunk's entry state and corrected values uc = U - W h, and leaves the
- *      final state in place;
+ *      chunk's entry state and corrected values uc = U - W h
+ *      (= T' (V - diag(exp(gc)) K h)), and leaves the final state in place;
  *   3. chunk_fwd_o: O = diag(exp(gc)) Q h_c + tril(decay * Q K^T) uc.
  * The arguments follow that page's launcher (gdn_prefill_fla's parameter
  * list): separate k/v head counts, packed strided rows, optional ragged
@@ -97,19 +99,26 @@ typedef struct gdn_varlen {
  *   slot(i, h, c) = cu_chunks[i]*nv + h*n_i + c,   n_i = chunks of sequence i
  * (dense: cu_chunks[i] = i*ceil(T/64), so slots run [B][nv][n_chunks]).
  * Regions (byte offsets from the scratch base, each 256-byte aligned):
- *   gc      float [slots][64]        chunk-local cumulative log-gate; rows past
- *                                    the sequence end repeat the last value
- *   w       float [slots][64][128]   W (rows past the end are 0)
- *   u       float [slots][64][128]   U (rows past the end are 0)
- *   s_entry bf16  [slots][128][128]  entry state of each chunk, [dk][dv]; for
- *                                    dense input this is [B][nv][T/64][dk][dv]
+ *   gc      float [slots][64]        chunk-local cumulative log-gate G_t; rows
+ *                                    past the sequence end repeat the last value
+ *   dec     float [slots][2][64]     exp(G_t), then exp(G_{n-1} - G_t)
+ *   tp      bf16  [slots][8][64][16] the UT transform T' = (I+L)^-1 diag(beta)
+ *                                    (so U = T' V, W = T' diag(exp(G)) K), as
+ *                                    bf16 hi/lo pairs in MFMA fragment order:
+ *                                    fragment f = 2*mt + kb, lane l = 16q + r
+ *                                    holds row t = 16mt + r, columns
+ *                                    s = 32kb + 4q + e (e = 0..3) and
+ *                                    s = 32kb + 16 + 4q + e, as 8 hi then 8 lo
+ *   s_entry bf16  [slots][128][128]  entry state of each chunk as S = h^T
+ *                                    ([dv][dk], the recurrence's orientation);
+ *                                    dense input: [B][nv][T/64][dv][dk]
  *   uc      bf16  [slots][128][64]   corrected values uc = U - W h, stored
  *                                    transposed ([dv][token])
  */
 typedef struct gdn_scratch_layout {
-  size_t gc, w, u, s_entry, uc; /* byte offsets */
-  size_t total;                 /* bytes needed */
-  int64_t slots;                /* chunk slots  */
+  size_t gc, dec, tp, s_entry, uc; /* byte offsets */
+  size_t total;                    /* bytes needed */
+  int64_t slots;                   /* chunk slots  */
 } gdn_scratch_layout;
 
 /* Scratch bytes for a problem (at least 256).  varlen NULL: dense B x T.

@@ -65,10 +65,10 @@ int layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen, gdn_s
   out->slots = slots;
   out->gc = off;
   off = align256(off + size_t(slots) * gdn::kGcBytes);
-  out->w = off;
-  off = align256(off + size_t(slots) * gdn::kWBytes);
-  out->u = off;
-  off = align256(off + size_t(slots) * gdn::kUBytes);
+  out->dec = off;
+  off = align256(off + size_t(slots) * gdn::kDecBytes);
+  out->tp = off;
+  off = align256(off + size_t(slots) * gdn::kTpBytes);
   out->s_entry = off;
   off = align256(off + size_t(slots) * gdn::kSBytes);
   out->uc = off;
@@ -154,8 +154,8 @@ gdn::Params make_params(const void *q, const void *k, const void *v, const float
   p.h_is_table = h_state_is_table;
   p.out = static_cast<uint16_t *>(out);
   p.gc = reinterpret_cast<float *>(base + lay.gc);
-  p.w = reinterpret_cast<float *>(base + lay.w);
-  p.u = reinterpret_cast<float *>(base + lay.u);
+  p.dec = reinterpret_cast<float *>(base + lay.dec);
+  p.tp = reinterpret_cast<uint16_t *>(base + lay.tp);
   p.s_entry = reinterpret_cast<uint16_t *>(base + lay.s_entry);
   p.uc = reinterpret_cast<uint16_t *>(base + lay.uc);
   p.qk_row = strides->qk_row;

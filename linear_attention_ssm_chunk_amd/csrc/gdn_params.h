@@ -13,11 +13,11 @@ constexpr int kDim = 128;     // dk = dv
 constexpr int kThreads = 256; // every kernel: 4 waves of 64
 
 // Bytes per chunk slot of each scratch region (see include/gdn_prefill.h).
-constexpr int64_t kGcBytes = int64_t(kChunk) * 4;
-constexpr int64_t kWBytes = int64_t(kChunk) * kDim * 4;
-constexpr int64_t kUBytes = int64_t(kChunk) * kDim * 4;
-constexpr int64_t kSBytes = int64_t(kDim) * kDim * 2;
-constexpr int64_t kUcBytes = int64_t(kDim) * kChunk * 2;
+constexpr int64_t kGcBytes = int64_t(kChunk) * 4;       // G_t
+constexpr int64_t kDecBytes = int64_t(2) * kChunk * 4;  // exp(G_t), exp(G_{n-1} - G_t)
+constexpr int64_t kTpBytes = int64_t(8) * 64 * 16 * 2;  // T' hi/lo fragments (16 KB)
+constexpr int64_t kSBytes = int64_t(kDim) * kDim * 2;   // entry state, bf16 [dv][dk]
+constexpr int64_t kUcBytes = int64_t(kDim) * kChunk * 2; // uc, bf16 [dv][t]
 
 struct Params {
   // inputs (bf16 as raw 16-bit patterns)
@@ -28,8 +28,8 @@ struct Params {
   int h_is_table;
   uint16_t *out; // bf16 [N_tok][nv][dv]
   // scratch regions
-  float *gc, *w, *u;
-  uint16_t *s_entry, *uc;
+  float *gc, *dec;
+  uint16_t *tp, *s_entry, *uc;
   int64_t qk_row, v_row, gb_row; // token-row pitches in elements
   int B, T, nk, nv;
   int n_chunks;                  // dense: ceil(T/64)

@@ -2,28 +2,35 @@
 //
 // Page "spark_model/layers/ops/ssm_gdn_a3.rs", doc comment of gdn_prefill_fla,
 // stage 1: per chunk and v-head, the chunk-local cumulative log-gate gc and the
-// solves (I+L) U = beta V, (I+L) W = beta exp(gc) K, with L sharing the key Gram
-// matrix's buffer (comment above smem_wu).  Here, for the chunk's n <= 64
+// WY/UT solves (I+L) U = beta V, (I+L) W = beta exp(gc) K, with L sharing the
+// key Gram matrix's buffer (comment above smem_wu).  For the chunk's n <= 64
 // tokens (rows past the sequence end are zero):
 //   G_r    = sum_{j<=r} g_j
 //   L[r,s] = beta_r exp(G_r - G_s) (k_r . k_s)        (s < r, else 0)
-//   T      = (I + L)^-1                               (unit lower triangular)
-//   U      = T diag(beta) V,   W = T diag(beta exp(G)) K
-// Work split of one 256-thread workgroup:
-//   wave 0      prefix sum of g (one lane per token)
-//   wave w      Gram tiles (w, 0..w) on bf16 MFMA -> L in LDS (f32)
-//   wave 0      T by forward substitution, one lane per column, f32
-//   wave w      W^T, U^T rows d in [32w, 32w+32): bf16 MFMA with K, V exact and
-//               T split hi+lo (two products), f32 out.
-// K and V are turned into k = token operands by identity products in
-// registers (see gdn_device.h), so the only LDS tile is L / T' (17 KB).
+//   T'     = (I + L)^-1 diag(beta)                     (the UT transform)
+// so that U = T' V and W = T' diag(exp(G)) K.  This stage emits T' itself
+// (16 KB per chunk-head) instead of W and U (64 KB in float32): the spine forms
+// uc = U - W h = T' (V - diag(exp(G)) K h) on the fly, which moves a third of
+// the bytes the three stages would otherwise move.
+//
+// One wave per (chunk, v-head):
+//   * lane t scans g; emits gc, exp(G_t) and exp(G_{n-1} - G_t);
+//   * the lower 10 tiles of K K^T on bf16 MFMA (K is exact in bf16) -> L (f32,
+//     LDS);
+//   * the two diagonal 32x32 blocks of T = (I+L)^-1 by f32 forward
+//     substitution, one lane per column (32 rows, <= 496 FMAs per lane);
+//   * the off-diagonal block T21 = -T22 (L21 T11) on MFMA, every operand split
+//     into bf16 hi + lo (three products each, ~2^-17 relative error);
+//   * T' = T diag(beta), split hi/lo, stored in the exact A-operand fragment
+//     order the spine reads (8 fragments x 64 lanes x 32 bytes).
 #include "gdn_device.h"
 
 namespace gdn {
 
-constexpr int kLP = 68; // row pitch (floats) of the L / T' tile
+constexpr int kLP = 68; // L / T tile pitch (floats)
+constexpr int kTP = 36; // T11 transposed pitch (floats)
 
-__global__ __launch_bounds__(kThreads) void chunk_cumsum_recompute_wu(Params p) {
+__global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
   const Seq s = seq_of(p, i);
   if (!s.ok || c >= s.nchunks) return;
@@ -31,15 +38,26 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_recompute_wu(Params p) 
   const int64_t slot = slot_of(p, s, h, c);
   const int kh = (h * p.nk) / p.nv;
   const int64_t row0 = s.tok0 + int64_t(c) * kChunk;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int q4 = lane >> 4, r16 = lane & 15;
 
   __shared__ __align__(16) float Ls[kChunk * kLP];
-  __shared__ float Gs[kChunk], Bs[kChunk], Es[kChunk];
+  __shared__ __align__(16) float Tt[32 * kTP];
+  __shared__ float Gs[kChunk], Bs[kChunk];
 
-  // --- gc: inclusive prefix sum of g over the chunk (g = 0 past the end, so
-  // padded rows repeat the last value) ---------------------------------------
-  if (wave == 0) {
+  // ---- K rows in the contiguous k order: kf[m][kb] = K[16m + r16][32kb + 8q .. +7]
+  const uint16_t *kbase = p.k + row0 * p.qk_row + int64_t(kh) * kDim;
+  bf16x8 kf[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = 16 * m + r16;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      kf[m][kb] = (t < n) ? load16_bf16x8(kbase + int64_t(t) * p.qk_row + 32 * kb + 8 * q4) : zero8();
+  }
+
+  // ---- gate: inclusive prefix sum over the chunk (g = 0 past the end) -----
+  {
     float gv = 0.f, bv = 0.f;
     if (lane < n) {
       const int64_t off = (row0 + lane) * p.gb_row + h;
@@ -52,96 +70,41 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_recompute_wu(Params p) 
       const float o = __shfl_up(G, d, 64);
       if (lane >= d) G += o;
     }
+    const float Gn = __shfl(G, n - 1, 64);
     Gs[lane] = G;
     Bs[lane] = bv;
-    Es[lane] = expf(G);
     p.gc[slot * kChunk + lane] = G;
+    p.dec[slot * 2 * kChunk + lane] = expf(G);
+    p.dec[slot * 2 * kChunk + kChunk + lane] = expf(Gn - G);
   }
 
-  // --- operands straight from HBM (16-byte loads, rows past the end = 0) ----
-  const uint16_t *kbase = p.k + row0 * p.qk_row + int64_t(kh) * kDim;
-  const uint16_t *vbase = p.v + row0 * p.v_row + int64_t(h) * kDim;
-  // kf[m][kb] = K[16m + r16][32kb + 8q .. +7]: B operands of the Gram
-  bf16x8 kf[4][4];
+  // ---- L = strict_lower(diag(beta) (D * K K^T)) ---------------------------
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int t = 16 * m + r16;
+  for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      kf[m][kb] = (t < n) ? load16_bf16x8(kbase + int64_t(t) * p.qk_row + 32 * kb + 8 * q4) : zero8();
-  }
-  // ka[kb]: A operands of this wave's Gram row tile (rows 16*wave + r16)
-  bf16x8 ka[4];
-  {
-    const int t = 16 * wave + r16;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      ka[kb] = (t < n) ? load16_bf16x8(kbase + int64_t(t) * p.qk_row + 32 * kb + 8 * q4) : zero8();
-  }
-  // this wave's 32 columns of K and V, natural orientation (for transposing)
-  bf16x8 kc[4], vc[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int t = 16 * m + r16;
-    const bool ok = t < n;
-    kc[m] = ok ? load16_bf16x8(kbase + int64_t(t) * p.qk_row + 32 * wave + 8 * q4) : zero8();
-    vc[m] = ok ? load16_bf16x8(vbase + int64_t(t) * p.v_row + 32 * wave + 8 * q4) : zero8();
-  }
-
-  __syncthreads(); // Gs, Bs, Es
-
-  // --- Gram row tile `wave`, column tiles 0..wave -> L --------------------
-#pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    if (ns <= wave) {
+    for (int ms = 0; ms <= mr; ++ms) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc = mfma(ka[kb], kf[ns][kb], acc);
-      const int sc = 16 * ns + r16; // C: column s, rows r
+      for (int kb = 0; kb < 4; ++kb) acc = mfma(kf[mr][kb], kf[ms][kb], acc);
+      const int sc = 16 * ms + r16; // C tile: column s, rows r
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int r = 16 * wave + 4 * q4 + ii;
+        const int r = 16 * mr + 4 * q4 + ii;
         Ls[r * kLP + sc] = (sc < r) ? Bs[r] * expf(Gs[r] - Gs[sc]) * acc[ii] : 0.f;
       }
     }
-  }
 
-  // --- K, V columns [32w, 32w+32) transposed in registers: kA[kb][b] is the
-  // A operand (rows d = 32w + 16b + r16, k = tokens, chain order) ------------
-  bf16x8 kA[2][2], vA[2][2];
+  // ---- diagonal blocks: T_bb = (I + L_bb)^-1, lane j owns column j of block
+  // b = j / 32:  T[r][j] = delta_rj - sum_{s<r} L[r][s] T[s][j] -------------
   {
-    const bf16x8 I0 = ident_contig(lane, 0), I1 = ident_contig(lane, 1);
-    f32x4 kt[4][2], vt[4][2];
+    const int b = lane >> 5, jj = lane & 31, base = 32 * b;
+    float t[32];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      kt[m][0] = mfma(kc[m], I0, zero4());
-      kt[m][1] = mfma(kc[m], I1, zero4());
-      vt[m][0] = mfma(vc[m], I0, zero4());
-      vt[m][1] = mfma(vc[m], I1, zero4());
-    }
+    for (int rr = 0; rr < 32; ++rr) {
+      float a0 = (rr == jj) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      const float *Lr = Ls + (base + rr) * kLP + base;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        kA[kb][b] = chain_frag(kt[2 * kb][b], kt[2 * kb + 1][b]);
-        vA[kb][b] = chain_frag(vt[2 * kb][b], vt[2 * kb + 1][b]);
-      }
-  }
-
-  __syncthreads(); // L complete
-
-  // --- T = (I + L)^-1 by forward substitution; lane j owns column j:
-  //     T[r][j] = delta_rj - sum_{s<r} L[r][s] T[s][j]
-  // then T' = T diag(beta) overwrites L in place (all reads of L are done). --
-  if (wave == 0) {
-    const int j = lane;
-    float t[kChunk];
-#pragma unroll
-    for (int r = 0; r < kChunk; ++r) {
-      float a0 = (r == j) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      const float *Lr = Ls + r * kLP;
-#pragma unroll
-      for (int s4 = 0; s4 < r / 4; ++s4) {
+      for (int s4 = 0; s4 < rr / 4; ++s4) {
         const f32x4 lv = *reinterpret_cast<const f32x4 *>(Lr + 4 * s4);
         a0 -= lv[0] * t[4 * s4 + 0];
         a1 -= lv[1] * t[4 * s4 + 1];
@@ -149,60 +112,98 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_recompute_wu(Params p) 
         a3 -= lv[3] * t[4 * s4 + 3];
       }
 #pragma unroll
-      for (int s1 = 4 * (r / 4); s1 < r; ++s1) a0 -= Lr[s1] * t[s1];
-      t[r] = (a0 + a1) + (a2 + a3);
+      for (int s1 = 4 * (rr / 4); s1 < rr; ++s1) a0 -= Lr[s1] * t[s1];
+      t[rr] = (a0 + a1) + (a2 + a3);
     }
-    const float bj = Bs[j];
+    // T11 and T22 row-major in place of L11 and L22 (their reads are done);
+    // T12 = 0; T11 also transposed for the B operand below.
 #pragma unroll
-    for (int r = 0; r < kChunk; ++r) Ls[r * kLP + j] = t[r] * bj;
+    for (int rr = 0; rr < 32; ++rr) Ls[(base + rr) * kLP + base + jj] = t[rr];
+    if (b == 1) {
+#pragma unroll
+      for (int rr = 0; rr < 32; ++rr) Ls[rr * kLP + 32 + jj] = 0.f;
+    } else {
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+        *reinterpret_cast<f32x4 *>(Tt + jj * kTP + 4 * a) =
+            f32x4{t[4 * a], t[4 * a + 1], t[4 * a + 2], t[4 * a + 3]};
+    }
   }
 
-  __syncthreads(); // T' ready
-
-  // --- W^T[d][t] = sum_s K^T[d][s] T''[t][s],  T'' = T' diag(exp(G));
-  //     U^T[d][t] = sum_s V^T[d][s] T'[t][s].
-  // C tile: column t = 16nt + r16, rows d = 32w + 16b + 4q .. +3 -> one float4
-  // store into row-major W[t][d]. ------------------------------------------
-  float *wout = p.w + slot * (kChunk * kDim);
-  float *uout = p.u + slot * (kChunk * kDim);
+  // ---- T21 = -T22 (L21 T11): rows 32..63, columns 0..31 -------------------
+  {
+    // Pm = L21 T11, contiguous k order over s in [0, 32)
+    f32x4 Pm[2][2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int t = 16 * nt + r16;
-    bf16x8 twh[2], twl[2], tuh[2], tul[2];
+    for (int mp = 0; mp < 2; ++mp) {
+      const float *ar = Ls + (32 + 16 * mp + r16) * kLP + 8 * q4;
+      const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
+      const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 4);
+      const float xa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      bf16x8 ah, al;
+      split8(xa, ah, al);
+#pragma unroll
+      for (int np = 0; np < 2; ++np) {
+        const float *br = Tt + (16 * np + r16) * kTP + 8 * q4;
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(br);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(br + 4);
+        const float xb[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        bf16x8 bh, bl;
+        split8(xb, bh, bl);
+        f32x4 acc = mfma(ah, bh, zero4());
+        acc = mfma(ah, bl, acc);
+        Pm[mp][np] = mfma(al, bh, acc);
+      }
+    }
+    // T21 = -T22 Pm; Pm's C tiles are the B operand in chain order over s'
+    bf16x8 ph[2], pl[2];
+#pragma unroll
+    for (int np = 0; np < 2; ++np) chain_split(Pm[0][np], Pm[1][np], ph[np], pl[np]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const float *ar = Ls + (32 + 16 * mt + r16) * kLP + 32 + 4 * q4;
+      const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
+      const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 16);
+      const float xa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      bf16x8 ah, al;
+      split8(xa, ah, al);
+#pragma unroll
+      for (int np = 0; np < 2; ++np) {
+        f32x4 acc = mfma(ah, ph[np], zero4());
+        acc = mfma(ah, pl[np], acc);
+        acc = mfma(al, ph[np], acc);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          Ls[(32 + 16 * mt + 4 * q4 + ii) * kLP + 16 * np + r16] = -acc[ii];
+      }
+    }
+  }
+
+  // ---- T' = T diag(beta) in the spine's A-operand order: fragment (mt, kb)
+  // holds rows t = 16mt + r16, columns s = 32kb + {4q..4q+3, 16+4q..16+4q+3},
+  // as 8 bf16 hi then 8 bf16 lo per lane -----------------------------------
+  uint16_t *tp = p.tp + slot * (8 * 64 * 16);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(Ls + t * kLP + 32 * kb + 4 * q4);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(Ls + t * kLP + 32 * kb + 16 + 4 * q4);
-      float xu[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      float xw[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sidx = 32 * kb + ((e < 4) ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
-        xw[e] = xu[e] * Es[sidx];
-      }
-      split8(xu, tuh[kb], tul[kb]);
-      split8(xw, twh[kb], twl[kb]);
+      const int t = 16 * mt + r16;
+      const int s0 = 32 * kb + 4 * q4, s1 = s0 + 16;
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(Ls + t * kLP + s0);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(Ls + t * kLP + s1);
+      const float x[8] = {a[0] * Bs[s0], a[1] * Bs[s0 + 1], a[2] * Bs[s0 + 2], a[3] * Bs[s0 + 3],
+                          b[0] * Bs[s1], b[1] * Bs[s1 + 1], b[2] * Bs[s1 + 2], b[3] * Bs[s1 + 3]};
+      bf16x8 hi, lo;
+      split8(x, hi, lo);
+      u32x4 *dst = reinterpret_cast<u32x4 *>(tp + ((mt * 2 + kb) * 64 + lane) * 16);
+      dst[0] = __builtin_bit_cast(u32x4, hi);
+      dst[1] = __builtin_bit_cast(u32x4, lo);
     }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x4 aw = zero4(), au = zero4();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        aw = mfma(kA[kb][b], twh[kb], aw);
-        aw = mfma(kA[kb][b], twl[kb], aw);
-        au = mfma(vA[kb][b], tuh[kb], au);
-        au = mfma(vA[kb][b], tul[kb], au);
-      }
-      const int d = 32 * wave + 16 * b + 4 * q4;
-      *reinterpret_cast<f32x4 *>(wout + t * kDim + d) = aw;
-      *reinterpret_cast<f32x4 *>(uout + t * kDim + d) = au;
-    }
-  }
 }
 
 hipError_t launch_stage1(const Params &p, hipStream_t stream) {
   dim3 grid(p.max_chunks, p.nv, p.B);
-  hipLaunchKernelGGL(chunk_cumsum_recompute_wu, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(chunk_cumsum_recompute_wu, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

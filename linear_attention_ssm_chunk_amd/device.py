@@ -136,8 +136,10 @@ class DeviceProblem:
         off = getattr(L, name)
         if name == "gc":
             return self.scratch[off:off + S * CHUNK * 4].view(torch.float32).view(S, CHUNK)
-        if name in ("w", "u"):
-            return self.scratch[off:off + S * CHUNK * HEAD_DIM * 4].view(torch.float32).view(S, CHUNK, HEAD_DIM)
+        if name == "dec":
+            return self.scratch[off:off + S * 2 * CHUNK * 4].view(torch.float32).view(S, 2, CHUNK)
+        if name == "tp":
+            return self.scratch[off:off + S * 8 * 64 * 16 * 2].view(torch.bfloat16).view(S, 8, 64, 16)
         if name == "s_entry":
             return self.scratch[off:off + S * HEAD_DIM * HEAD_DIM * 2].view(torch.bfloat16).view(S, HEAD_DIM, HEAD_DIM)
         if name == "uc":

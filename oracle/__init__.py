@@ -34,6 +34,7 @@ from .chunked import (  # noqa: F401
     chunk_cumsum,
     gram_strict_lower,
     wy_solve,
+    ut_transform,
     spine_step,
     chunk_output,
     gdn_chunked,

@@ -8,7 +8,9 @@ The page "spark_model/layers/ops/ssm_gdn_a3.rs" (doc comment of
 1. recompute_wu: the chunk-local cumulative log-gate ``gc``; the strictly
    lower matrix ``L`` that shares its buffer with the key Gram matrix ("L
    aliases the kk Gram (disjoint triangles)", comment above ``smem_wu``); the
-   solves ``(I+L) U = beta V`` and ``(I+L) W = beta exp(gc) K``.
+   solves ``(I+L) U = beta V`` and ``(I+L) W = beta exp(gc) K``.  The same
+   solves written as one matrix, the UT transform ``T' = (I+L)^-1 diag(beta)``
+   (``U = T' V``, ``W = T' diag(exp(gc)) K``), is ``ut_transform``.
 2. chunk_delta_h: a serial pass over chunks that emits each chunk's entry
    state and its corrected values ``uc``, and updates the state in place.
 3. chunk_fwd_o: ``O = Q~ S_c + tril(decay * Q~ K^T) uc`` per chunk.
@@ -86,6 +88,19 @@ def wy_solve(L, k_c, v_c, beta_c, G):
     return W, U
 
 
+def ut_transform(L, beta_c):
+    """Stage 1, the UT transform: ``T' = (I+L)^-1 diag(beta)``, the matrix that
+    maps the right-hand sides of the WY/UT solves to their solutions:
+    ``U = T' V`` and ``W = T' diag(exp(G)) K``.  L [nv, n, n], beta_c [n, nv]
+    -> T' [nv, n, n] (lower triangular)."""
+    beta_c = np.asarray(beta_c, dtype=np.float64)
+    nv, n = L.shape[0], L.shape[1]
+    out = np.empty((nv, n, n))
+    for h in range(nv):
+        out[h] = solve_triangular(np.eye(n) + L[h], np.diag(beta_c[:, h]), lower=True, unit_diagonal=True)
+    return out
+
+
 def spine_step(h, W, U, k_c, G):
     """Stage 2, one chunk of the serial spine.  ``h`` [nv, dk, dv] is the
     chunk's entry state.  Returns (uc [nv, n, dv], h_next [nv, dk, dv]) with
@@ -116,8 +131,9 @@ def gdn_chunked(q, k, v, g, beta, h0, chunk=64, keep_intermediates=False):
     """One sequence through the three stages.  Arguments as
     ``recurrence.gdn_recurrence``.  Returns (o, h_final, entry, inter) where
     ``inter`` is None or, with ``keep_intermediates``, a list over chunks of
-    dicts with ``gc`` [n, nv], ``W`` [nv, n, dk], ``U`` [nv, n, dv] and
-    ``uc`` [nv, n, dv] (n = tokens in that chunk)."""
+    dicts with ``gc`` [n, nv], ``W`` [nv, n, dk], ``U`` [nv, n, dv],
+    ``Tp`` (the UT transform T') [nv, n, n] and ``uc`` [nv, n, dv]
+    (n = tokens in that chunk)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -141,6 +157,6 @@ def gdn_chunked(q, k, v, g, beta, h0, chunk=64, keep_intermediates=False):
         uc, h_next = spine_step(h, W, U, k_c, G)
         o[sl] = chunk_output(q_c, k_c, G, h, uc)
         if inter is not None:
-            inter.append({"gc": G, "W": W, "U": U, "uc": uc})
+            inter.append({"gc": G, "W": W, "U": U, "Tp": ut_transform(L, beta[sl]), "uc": uc})
         h = h_next
     return o, h, entry, inter

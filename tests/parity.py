@@ -6,8 +6,10 @@ Tolerances (written here once, used by every parity test):
   * entry states (bf16): max abs <= 2e-2, relative Frobenius <= 4e-3
     (bf16 storage alone is ~2^-9 relative)
   * gc: |err| <= 1e-4 * (1 + |G|)   (64 float32 additions)
-  * W, U (float32): relative Frobenius <= 1e-4 per slot (hi/lo bf16 products
-    carry ~2^-17 relative error)
+  * decays exp(G_t), exp(G_{n-1} - G_t): relative error <= 1e-4
+  * T' (hi + lo bf16 pair, ~2^-17): relative Frobenius <= 1e-4 per slot; W and
+    U rebuilt from it (U = T' V, W = T' diag(exp(G)) K): <= 1e-4 against the
+    oracle's direct triangular solves
   * uc (bf16): relative Frobenius <= 8e-3 per slot
 """
 
@@ -21,12 +23,39 @@ TOL_STATE_RELFRO = 1e-3
 TOL_ENTRY_MAXABS = 2e-2
 TOL_ENTRY_RELFRO = 4e-3
 TOL_WU_RELFRO = 1e-4
+TOL_TP_RELFRO = 1e-4
 TOL_UC_RELFRO = 8e-3
 
 
 def relfro(a, b):
     nb = np.linalg.norm(b)
     return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def _tp_index():
+    t = np.zeros((8, 64, 8), dtype=np.int64)
+    sc = np.zeros((8, 64, 8), dtype=np.int64)
+    for mt in range(4):
+        for kb in range(2):
+            for lane in range(64):
+                q, r = lane // 16, lane % 16
+                for e in range(8):
+                    t[2 * mt + kb, lane, e] = 16 * mt + r
+                    sc[2 * mt + kb, lane, e] = 32 * kb + (4 * q + e if e < 4 else 16 + 4 * q + e - 4)
+    return t, sc
+
+
+_TP_T, _TP_S = _tp_index()
+
+
+def unpack_tp(frags):
+    """T' [64, 64] from the documented fragment layout [8][64][16]: fragment
+    2*mt + kb, lane 16q + r holds row 16mt + r, columns 32kb + 4q + e and
+    32kb + 16 + 4q + e (e = 0..3), 8 bf16 hi then 8 bf16 lo."""
+    f = np.asarray(frags, dtype=np.float64)
+    T = np.zeros((64, 64))
+    T[_TP_T, _TP_S] = f[..., :8] + f[..., 8:]
+    return T
 
 
 def seq_arrays(p, i, heads=None):
@@ -48,12 +77,12 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
     out = dp.output()
     state = dp.state()
     worst = dict(o_maxabs=0.0, state_relfro=0.0, entry_maxabs=0.0, entry_relfro=0.0,
-                 w_relfro=0.0, u_relfro=0.0, uc_relfro=0.0, gc_err=0.0)
+                 w_relfro=0.0, u_relfro=0.0, tp_relfro=0.0, dec_err=0.0, uc_relfro=0.0, gc_err=0.0)
     regions = {}
     if entries or intermediates:
         regions["s_entry"] = dp.region("s_entry")
     if intermediates:
-        for r in ("gc", "w", "u", "uc"):
+        for r in ("gc", "dec", "tp", "uc"):
             regions[r] = dp.region(r)
     for i in seqs:
         a = int(p.cu_seqlens[i])
@@ -72,7 +101,8 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
             for c in range(ent_ref.shape[0]):
                 sl = dp.slot(i, h, c)
                 if "s_entry" in regions:
-                    s_gpu = regions["s_entry"][sl].float().cpu().numpy().astype(np.float64)
+                    # stored as S = h^T ([dv][dk])
+                    s_gpu = regions["s_entry"][sl].float().cpu().numpy().astype(np.float64).T
                     worst["entry_maxabs"] = max(worst["entry_maxabs"], float(np.abs(s_gpu - ent_ref[c, j]).max()))
                     worst["entry_relfro"] = max(worst["entry_relfro"], relfro(s_gpu, ent_ref[c, j]))
                 if intermediates:
@@ -83,11 +113,21 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
                     worst["gc_err"] = max(worst["gc_err"], float((np.abs(gc_gpu[:n] - G) / (1 + np.abs(G))).max()))
                     # rows past the end repeat the last value
                     worst["gc_err"] = max(worst["gc_err"], float(np.abs(gc_gpu[n:] - G[-1]).max(initial=0)))
-                    w_gpu = regions["w"][sl].cpu().numpy().astype(np.float64)
-                    u_gpu = regions["u"][sl].cpu().numpy().astype(np.float64)
-                    worst["w_relfro"] = max(worst["w_relfro"], relfro(w_gpu[:n], d["W"][j]))
-                    worst["u_relfro"] = max(worst["u_relfro"], relfro(u_gpu[:n], d["U"][j]))
-                    assert np.all(w_gpu[n:] == 0) and np.all(u_gpu[n:] == 0), "padded W/U rows must be 0"
+                    dec = regions["dec"][sl].cpu().numpy().astype(np.float64)
+                    eg_ref = np.exp(G)
+                    dn_ref = np.exp(G[-1] - G)
+                    # relative, with an absolute floor below float32's normal range
+                    worst["dec_err"] = max(worst["dec_err"],
+                                           float((np.abs(dec[0, :n] - eg_ref) / (eg_ref + 1e-33)).max()),
+                                           float((np.abs(dec[1, :n] - dn_ref) / (dn_ref + 1e-33)).max()))
+                    Tp = unpack_tp(regions["tp"][sl].float().cpu().numpy())
+                    assert np.all(Tp[n:] == 0) and np.all(Tp[:, n:] == 0), "padded rows/columns of T' must be 0"
+                    Tp = Tp[:n, :n]
+                    worst["tp_relfro"] = max(worst["tp_relfro"], relfro(Tp, d["Tp"][j]))
+                    kk = arrs["k"][64 * c:64 * c + n, j]
+                    vv = arrs["v"][64 * c:64 * c + n, j]
+                    worst["w_relfro"] = max(worst["w_relfro"], relfro(Tp @ (np.exp(G)[:, None] * kk), d["W"][j]))
+                    worst["u_relfro"] = max(worst["u_relfro"], relfro(Tp @ vv, d["U"][j]))
                     uc_gpu = regions["uc"][sl].float().cpu().numpy().astype(np.float64).T  # [t][dv]
                     worst["uc_relfro"] = max(worst["uc_relfro"], relfro(uc_gpu[:n], d["uc"][j]))
     if report is not None:
@@ -103,6 +143,8 @@ def assert_within(worst, intermediates=False, entries=True):
         assert worst["entry_relfro"] <= TOL_ENTRY_RELFRO, worst
     if intermediates:
         assert worst["gc_err"] <= 1e-4, worst
+        assert worst["dec_err"] <= 1e-4, worst
+        assert worst["tp_relfro"] <= TOL_TP_RELFRO, worst
         assert worst["w_relfro"] <= TOL_WU_RELFRO, worst
         assert worst["u_relfro"] <= TOL_WU_RELFRO, worst
         assert worst["uc_relfro"] <= TOL_UC_RELFRO, worst

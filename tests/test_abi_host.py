@@ -122,9 +122,9 @@ def test_scratch_layout_arithmetic():
     L = B.gdn_prefill_scratch_layout(4, 8192, 32, 128, 128)
     slots = 4 * 128 * 32
     assert L.slots == slots and L.gc == 0
-    assert L.w == slots * 64 * 4
-    assert L.u == L.w + slots * 64 * 128 * 4
-    assert L.s_entry == L.u + slots * 64 * 128 * 4
+    assert L.dec == slots * 64 * 4
+    assert L.tp == L.dec + slots * 2 * 64 * 4
+    assert L.s_entry == L.tp + slots * 8 * 64 * 16 * 2
     assert L.uc == L.s_entry + slots * 128 * 128 * 2
     assert L.total == L.uc + slots * 128 * 64 * 2
     assert B.gdn_prefill_scratch_bytes(2, 0, 4, 128, 128, B.gdn_varlen(P, P, 0, 0)) == 256

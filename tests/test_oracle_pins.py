@@ -336,3 +336,22 @@ def _output_without_entry_decay(q_c, k_c, G, h, uc):
     Kh = np.transpose(k_c, (1, 0, 2))
     P = chunked_mod._decay_lower(G, True) * np.matmul(Qh, np.transpose(Kh, (0, 2, 1)))
     return np.transpose(np.matmul(Qh, h) + np.matmul(P, uc), (1, 0, 2))
+
+
+def test_ut_transform_reproduces_the_direct_solves():
+    """T' = (I+L)^-1 diag(beta) maps the right-hand sides to the solutions of
+    the direct triangular solves: U = T' V and W = T' diag(exp(G)) K; and
+    (I+L) T' = diag(beta) holds to rounding."""
+    rng = np.random.default_rng(31)
+    q, k, v, g, beta, h0 = rand_problem(rng, 64, 1, 3, 128, 128)
+    kap = kv_head_map(1, 3)
+    k_c = k[:, kap]
+    G = chunked_mod.chunk_cumsum(g)
+    L = chunked_mod.gram_strict_lower(k_c, beta, G)
+    W, U = chunked_mod.wy_solve(L, k_c, v, beta, G)
+    Tp = chunked_mod.ut_transform(L, beta)
+    for h in range(3):
+        assert rel(Tp[h] @ v[:, h], U[h]) < 1e-12
+        assert rel(Tp[h] @ (np.exp(G[:, h])[:, None] * k_c[:, h]), W[h]) < 1e-12
+        assert rel((np.eye(64) + L[h]) @ Tp[h], np.diag(beta[:, h])) < 1e-12
+        assert np.all(np.triu(Tp[h], 1) == 0)
