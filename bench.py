@@ -43,11 +43,11 @@ def algorithmic(p):
     """Per-kernel algorithmic bytes and flops for problem p (inputs.Problem).
 
     Bytes: every operand each stage must read or write once (q, k counted once
-    per k-head).  Stage 1 reads k, g, beta and writes gc, the decays and T'
-    (16 KB per chunk-head); stage 2 reads T', k, v, the decays and the state
-    and writes the entry states (32 KB per chunk-head), uc (16 KB) and the
-    state; stage 3 reads q, k, gc, the decays, the entry states and uc and
-    writes o.  Flops: dense-tile MFMA work per chunk-head."""
+    per k-head).  Stage 1 reads k, g, beta and writes gc, the decays, T' (16
+    KB per chunk-head) and K, K^T fragments (32 KB per chunk and k-head); stage 2
+    reads T', the K fragments, v, the decays and the state and writes the entry states
+    (32 KB per chunk-head), uc (16 KB) and the state; stage 3 reads q, k, gc,
+    the decays, the entry states and uc and writes o.  Flops: dense-tile MFMA work per chunk-head."""
     N, nk, nv = p.n_tokens, p.nk, p.nv
     slots = int(p.cu_chunks[-1]) * nv
     nseq = p.nseq
@@ -63,9 +63,10 @@ def algorithmic(p):
     uc_bytes = slots * d * C * 2
     state_bytes = nseq * nv * d * d * 4
     o_bytes = N * nv * d * 2
+    kt_bytes = int(p.cu_chunks[-1]) * nk * C * d * 2 * 2   # K and K^T fragments, once per k-head
     by = {
-        1: k_bytes + gb_bytes + gc_bytes + dec_bytes + tp_bytes,
-        2: tp_bytes + k_bytes + v_bytes + dec_bytes + 2 * state_bytes + s_bytes + uc_bytes,
+        1: k_bytes + gb_bytes + gc_bytes + dec_bytes + tp_bytes + kt_bytes,
+        2: tp_bytes + kt_bytes + v_bytes + dec_bytes + 2 * state_bytes + s_bytes + uc_bytes,
         3: q_bytes + k_bytes + gc_bytes + dec_bytes // 2 + s_bytes + uc_bytes + o_bytes,
     }
     # Gram 2C^2 d; spine K h, T' R, K^T uc: 2Cd^2 + 2C^2 d + 2Cd^2; output

@@ -102,31 +102,40 @@ typedef struct gdn_varlen {
  *   gc      float [slots][64]        chunk-local cumulative log-gate G_t; rows
  *                                    past the sequence end repeat the last value
  *   dec     float [slots][2][64]     exp(G_t), then exp(G_{n-1} - G_t)
- *   tp      bf16  [slots][8][64][16] the UT transform T' = (I+L)^-1 diag(beta)
- *                                    (so U = T' V, W = T' diag(exp(G)) K), as
- *                                    bf16 hi/lo pairs in MFMA fragment order:
- *                                    fragment f = 2*mt + kb, lane l = 16q + r
- *                                    holds row t = 16mt + r, columns
- *                                    s = 32kb + 4q + e (e = 0..3) and
- *                                    s = 32kb + 16 + 4q + e, as 8 hi then 8 lo
+ *   tp      bf16  [slots][2][8][64][8] the UT transform T' = (I+L)^-1 diag(beta)
+ *                                    (so U = T' V, W = T' diag(exp(G)) K) as
+ *                                    bf16 hi (index 0) and lo (index 1) parts
+ *                                    in MFMA fragment order: fragment
+ *                                    f = 2*mt + kb, lane l = 16q + r holds row
+ *                                    t = 16mt + r, columns s = 32kb + 4q + e
+ *                                    (e = 0..3) and s = 32kb + 16 + 4q + e
  *   s_entry bf16  [slots][128][128]  entry state of each chunk as S = h^T
  *                                    ([dv][dk], the recurrence's orientation);
  *                                    dense input: [B][nv][T/64][dv][dk]
  *   uc      bf16  [slots][128][64]   corrected values uc = U - W h, stored
  *                                    transposed ([dv][token])
+ *   kfr     bf16  [kslots][2][16][64][8] K of each (sequence, k-head, chunk)
+ *                                    in two MFMA fragment orders; kslot(i, kh, c)
+ *                                    = cu_chunks[i]*nk + kh*n_i + c.  Index 0,
+ *                                    fragment f = 4*mt + kb, lane 16q + r:
+ *                                    K[16mt + r][32kb + 4q + e] and
+ *                                    K[16mt + r][32kb + 16 + 4q + e]; index 1,
+ *                                    fragment f = 2*m + kb: K[32kb + 4q + e][16m + r]
+ *                                    and K[32kb + 16 + 4q + e][16m + r] (e = 0..3)
  */
 typedef struct gdn_scratch_layout {
-  size_t gc, dec, tp, s_entry, uc; /* byte offsets */
+  size_t gc, dec, tp, s_entry, uc, kfr; /* byte offsets */
   size_t total;                    /* bytes needed */
   int64_t slots;                   /* chunk slots  */
 } gdn_scratch_layout;
 
 /* Scratch bytes for a problem (at least 256).  varlen NULL: dense B x T.
  * Returns 0 if the sizes are invalid. */
-size_t gdn_prefill_scratch_bytes(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen);
+size_t gdn_prefill_scratch_bytes(int B, int T, int nk, int nv, int dk, int dv,
+                                 const gdn_varlen *varlen);
 
 /* Fill *out with the scratch layout above.  Returns GDN_OK or an error. */
-int gdn_prefill_scratch_layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen,
+int gdn_prefill_scratch_layout(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen,
                                gdn_scratch_layout *out);
 
 /*

@@ -34,7 +34,8 @@ class gdn_varlen(ctypes.Structure):
 
 class gdn_scratch_layout(ctypes.Structure):
     _fields_ = [("gc", ctypes.c_size_t), ("dec", ctypes.c_size_t), ("tp", ctypes.c_size_t),
-                ("s_entry", ctypes.c_size_t), ("uc", ctypes.c_size_t), ("total", ctypes.c_size_t),
+                ("s_entry", ctypes.c_size_t), ("uc", ctypes.c_size_t), ("kfr", ctypes.c_size_t),
+                ("total", ctypes.c_size_t),
                 ("slots", ctypes.c_int64)]
 
 
@@ -63,9 +64,9 @@ def lib():
         L.gdn_prefill_stage.restype = i32
         L.gdn_prefill_validate.argtypes = common
         L.gdn_prefill_validate.restype = i32
-        L.gdn_prefill_scratch_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen)]
+        L.gdn_prefill_scratch_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen)]
         L.gdn_prefill_scratch_bytes.restype = sz
-        L.gdn_prefill_scratch_layout.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen),
+        L.gdn_prefill_scratch_layout.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen),
                                                  ctypes.POINTER(gdn_scratch_layout)]
         L.gdn_prefill_scratch_layout.restype = i32
         L.gdn_varlen_check_host.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
@@ -144,15 +145,15 @@ def gdn_prefill_validate(q, k, v, g, beta, h_state, h_state_is_table, out, scrat
     return lib().gdn_prefill_validate(*args)
 
 
-def gdn_prefill_scratch_bytes(B, T, nv, dk, dv, varlen=None):
+def gdn_prefill_scratch_bytes(B, T, nk, nv, dk, dv, varlen=None):
     vl = _varlen(varlen)
-    return lib().gdn_prefill_scratch_bytes(B, T, nv, dk, dv, _ref(vl))
+    return lib().gdn_prefill_scratch_bytes(B, T, nk, nv, dk, dv, _ref(vl))
 
 
-def gdn_prefill_scratch_layout(B, T, nv, dk, dv, varlen=None):
+def gdn_prefill_scratch_layout(B, T, nk, nv, dk, dv, varlen=None):
     vl = _varlen(varlen)
     out = gdn_scratch_layout()
-    rc = lib().gdn_prefill_scratch_layout(B, T, nv, dk, dv, _ref(vl), ctypes.byref(out))
+    rc = lib().gdn_prefill_scratch_layout(B, T, nk, nv, dk, dv, _ref(vl), ctypes.byref(out))
     if rc != GDN_OK:
         raise GdnError(rc, gdn_last_error())
     return out

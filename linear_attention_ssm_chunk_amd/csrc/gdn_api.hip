@@ -52,10 +52,11 @@ int64_t chunk_slots(int B, int T, const gdn_varlen *varlen) {
   return int64_t(B) * ((int64_t(T) + GDN_CHUNK - 1) / GDN_CHUNK);
 }
 
-int layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen, gdn_scratch_layout *out) {
+int layout(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen, gdn_scratch_layout *out) {
   if (dk != GDN_HEAD_DIM || dv != GDN_HEAD_DIM)
     return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
-  if (nv <= 0) return fail(GDN_EINVAL, "nv=%d must be positive", nv);
+  if (nv <= 0 || nk <= 0 || nv % nk != 0)
+    return fail(GDN_EINVAL, "head counts: nk=%d nv=%d (nv must be a positive multiple of nk)", nk, nv);
   const int64_t chunks = chunk_slots(B, T, varlen);
   if (chunks < 0)
     return fail(GDN_EINVAL, "sizes: B=%d T=%d%s give no valid chunk count", B, T,
@@ -73,6 +74,8 @@ int layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen, gdn_s
   off = align256(off + size_t(slots) * gdn::kSBytes);
   out->uc = off;
   off = align256(off + size_t(slots) * gdn::kUcBytes);
+  out->kfr = off;
+  off = align256(off + size_t(chunks) * nk * gdn::kKfrBytes);
   out->total = off > 256 ? off : 256; // never 0 for a valid problem
   return ok();
 }
@@ -132,7 +135,7 @@ int validate(const void *q, const void *k, const void *v, const float *g, const 
     if (int64_t(varlen->total_chunks) * GDN_CHUNK < int64_t(T))
       return fail(GDN_EINVAL, "ragged: total_chunks=%d cannot hold T=%d tokens", varlen->total_chunks, T);
   }
-  int rc = layout(B, T, nv, dk, dv, varlen, lay);
+  int rc = layout(B, T, nk, nv, dk, dv, varlen, lay);
   if (rc != GDN_OK) return rc;
   if (scratch_bytes < lay->total)
     return fail(GDN_ESCRATCH, "scratch: %zu bytes given, %zu needed", scratch_bytes, lay->total);
@@ -158,6 +161,7 @@ gdn::Params make_params(const void *q, const void *k, const void *v, const float
   p.tp = reinterpret_cast<uint16_t *>(base + lay.tp);
   p.s_entry = reinterpret_cast<uint16_t *>(base + lay.s_entry);
   p.uc = reinterpret_cast<uint16_t *>(base + lay.uc);
+  p.kfr = reinterpret_cast<uint16_t *>(base + lay.kfr);
   p.qk_row = strides->qk_row;
   p.v_row = strides->v_row;
   p.gb_row = strides->gb_row;
@@ -197,16 +201,16 @@ int run_stage(int stage, const gdn::Params &p, hipStream_t stream) {
 
 extern "C" {
 
-size_t gdn_prefill_scratch_bytes(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen) {
+size_t gdn_prefill_scratch_bytes(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen) {
   gdn_scratch_layout lay;
-  if (layout(B, T, nv, dk, dv, varlen, &lay) != GDN_OK) return 0;
+  if (layout(B, T, nk, nv, dk, dv, varlen, &lay) != GDN_OK) return 0;
   return lay.total;
 }
 
-int gdn_prefill_scratch_layout(int B, int T, int nv, int dk, int dv, const gdn_varlen *varlen,
+int gdn_prefill_scratch_layout(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen,
                                gdn_scratch_layout *out) {
   if (!out) return fail(GDN_EINVAL, "null pointer: layout output is required");
-  return layout(B, T, nv, dk, dv, varlen, out);
+  return layout(B, T, nk, nv, dk, dv, varlen, out);
 }
 
 int gdn_prefill_validate(const void *q, const void *k, const void *v, const float *g, const float *beta,

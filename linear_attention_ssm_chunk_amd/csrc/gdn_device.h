@@ -43,46 +43,50 @@ __device__ __forceinline__ bf16x8 zero8() {
 }
 
 // float -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, to_bf16(x));
+// Two floats -> one register of two bf16 (a in the low half), one instruction.
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// Split two floats into hi = bf16(x) and lo = bf16(x - hi), packed in pairs:
+// hi + lo carries about 16 mantissa bits, so a product of split operands done
+// as hi*hi + hi*lo + lo*hi keeps ~2^-17 relative error with bf16 MFMA.
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = cvt_pk(a, b);
+  const float ha = __builtin_bit_cast(float, hi << 16);
+  const float hb = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+  lo = cvt_pk(a - ha, b - hb);
 }
 
 // Pack four floats (consecutive elements of one lane) as 4 bf16 = 8 bytes.
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
-  return u32x2{f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
-               f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16)};
+  return u32x2{cvt_pk(a, b), cvt_pk(c, d)};
 }
 
 // Chain-order fragment from two C tiles (tile for k 0..15 and k 16..31).
 __device__ __forceinline__ bf16x8 chain_frag(const f32x4 &lo_tile, const f32x4 &hi_tile) {
-  bf16x8 f;
-  f[0] = to_bf16(lo_tile[0]); f[1] = to_bf16(lo_tile[1]);
-  f[2] = to_bf16(lo_tile[2]); f[3] = to_bf16(lo_tile[3]);
-  f[4] = to_bf16(hi_tile[0]); f[5] = to_bf16(hi_tile[1]);
-  f[6] = to_bf16(hi_tile[2]); f[7] = to_bf16(hi_tile[3]);
-  return f;
+  return __builtin_bit_cast(bf16x8, u32x4{cvt_pk(lo_tile[0], lo_tile[1]), cvt_pk(lo_tile[2], lo_tile[3]),
+                                          cvt_pk(hi_tile[0], hi_tile[1]), cvt_pk(hi_tile[2], hi_tile[3])});
 }
 
-// Split eight floats into hi = bf16(x) and lo = bf16(x - hi): hi + lo carries
-// about 16 mantissa bits, so a product of two split operands done as
-// hi*hi + hi*lo + lo*hi keeps ~2^-17 relative error with bf16 MFMA.
+// Split eight floats into hi/lo bf16 fragments (see split_pk).
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    __bf16 h = to_bf16(x[e]);
-    hi[e] = h;
-    lo[e] = to_bf16(x[e] - (float)h);
-  }
+  for (int e = 0; e < 4; ++e) split_pk(x[2 * e], x[2 * e + 1], h[e], l[e]);
+  hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
 // Chain-order split fragment from two C tiles.
 __device__ __forceinline__ void chain_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi,
                                             bf16x8 &lo) {
-  float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
   split8(x, hi, lo);
 }
 

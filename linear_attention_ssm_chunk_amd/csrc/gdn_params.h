@@ -18,6 +18,7 @@ constexpr int64_t kDecBytes = int64_t(2) * kChunk * 4;  // exp(G_t), exp(G_{n-1}
 constexpr int64_t kTpBytes = int64_t(8) * 64 * 16 * 2;  // T' hi/lo fragments (16 KB)
 constexpr int64_t kSBytes = int64_t(kDim) * kDim * 2;   // entry state, bf16 [dv][dk]
 constexpr int64_t kUcBytes = int64_t(kDim) * kChunk * 2; // uc, bf16 [dv][t]
+constexpr int64_t kKfrBytes = int64_t(2) * kDim * kChunk * 2; // K and K^T fragments, per k-head
 
 struct Params {
   // inputs (bf16 as raw 16-bit patterns)
@@ -29,7 +30,7 @@ struct Params {
   uint16_t *out; // bf16 [N_tok][nv][dv]
   // scratch regions
   float *gc, *dec;
-  uint16_t *tp, *s_entry, *uc;
+  uint16_t *tp, *s_entry, *uc, *kfr;
   int64_t qk_row, v_row, gb_row; // token-row pitches in elements
   int B, T, nk, nv;
   int n_chunks;                  // dense: ceil(T/64)

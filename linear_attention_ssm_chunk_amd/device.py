@@ -91,11 +91,13 @@ class DeviceProblem:
         self.reset_state()
 
         self.out = torch.empty((self.N, self.nv, HEAD_DIM), dtype=torch.bfloat16, device=device)
-        self.scratch_bytes = B.gdn_prefill_scratch_bytes(self.B, self.T, self.nv, HEAD_DIM, HEAD_DIM, self.varlen)
+        self.scratch_bytes = B.gdn_prefill_scratch_bytes(self.B, self.T, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
+                                                         self.varlen)
         if self.scratch_bytes == 0:
             raise ValueError("invalid sizes for the scratch layout")
         self.scratch = torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
-        self.layout_info = B.gdn_prefill_scratch_layout(self.B, self.T, self.nv, HEAD_DIM, HEAD_DIM, self.varlen)
+        self.layout_info = B.gdn_prefill_scratch_layout(self.B, self.T, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
+                                                        self.varlen)
 
     # -- state ---------------------------------------------------------------
     def reset_state(self):
@@ -139,7 +141,7 @@ class DeviceProblem:
         if name == "dec":
             return self.scratch[off:off + S * 2 * CHUNK * 4].view(torch.float32).view(S, 2, CHUNK)
         if name == "tp":
-            return self.scratch[off:off + S * 8 * 64 * 16 * 2].view(torch.bfloat16).view(S, 8, 64, 16)
+            return self.scratch[off:off + S * 2 * 8 * 64 * 8 * 2].view(torch.bfloat16).view(S, 2, 8, 64, 8)
         if name == "s_entry":
             return self.scratch[off:off + S * HEAD_DIM * HEAD_DIM * 2].view(torch.bfloat16).view(S, HEAD_DIM, HEAD_DIM)
         if name == "uc":

@@ -49,12 +49,12 @@ _TP_T, _TP_S = _tp_index()
 
 
 def unpack_tp(frags):
-    """T' [64, 64] from the documented fragment layout [8][64][16]: fragment
-    2*mt + kb, lane 16q + r holds row 16mt + r, columns 32kb + 4q + e and
-    32kb + 16 + 4q + e (e = 0..3), 8 bf16 hi then 8 bf16 lo."""
+    """T' [64, 64] from the documented fragment layout [2][8][64][8]: part 0
+    hi, part 1 lo; fragment 2*mt + kb, lane 16q + r holds row 16mt + r,
+    columns 32kb + 4q + e and 32kb + 16 + 4q + e (e = 0..3)."""
     f = np.asarray(frags, dtype=np.float64)
     T = np.zeros((64, 64))
-    T[_TP_T, _TP_S] = f[..., :8] + f[..., 8:]
+    T[_TP_T, _TP_S] = f[0] + f[1]
     return T
 
 

@@ -46,7 +46,8 @@ def good_args(**over):
              B=2, T=200, nk=2, nv=4, dk=128, dv=128, strides=(2 * 128, 4 * 128, 4), varlen=None)
     a.update(over)
     if a["scratch_bytes"] is None:
-        a["scratch_bytes"] = B.gdn_prefill_scratch_bytes(a["B"], a["T"], a["nv"], 128, 128, a["varlen"]) or 1
+        a["scratch_bytes"] = B.gdn_prefill_scratch_bytes(a["B"], a["T"], max(a["nk"], 1), a["nv"], 128, 128,
+                                                         a["varlen"]) or 1
     return a
 
 
@@ -94,7 +95,7 @@ def test_each_guard_rejects_by_name(over, code, needle):
 
 def test_ragged_guards():
     vl = B.gdn_varlen(P + 64, P + 128, 3, 5)
-    rc, msg = validate(varlen=vl, T=300, scratch_bytes=B.gdn_prefill_scratch_bytes(2, 300, 4, 128, 128, vl))
+    rc, msg = validate(varlen=vl, T=300, scratch_bytes=B.gdn_prefill_scratch_bytes(2, 300, 2, 4, 128, 128, vl))
     assert rc == B.GDN_OK, msg
     rc, msg = validate(varlen=B.gdn_varlen(0, P + 128, 3, 5), T=300)
     assert rc == B.GDN_EINVAL and "cu_seqlens and cu_chunks" in msg
@@ -119,21 +120,24 @@ def test_prefill_rejects_without_touching_the_gpu():
 
 
 def test_scratch_layout_arithmetic():
-    L = B.gdn_prefill_scratch_layout(4, 8192, 32, 128, 128)
-    slots = 4 * 128 * 32
+    L = B.gdn_prefill_scratch_layout(4, 8192, 16, 32, 128, 128)
+    chunks = 4 * 128
+    slots = chunks * 32
     assert L.slots == slots and L.gc == 0
     assert L.dec == slots * 64 * 4
     assert L.tp == L.dec + slots * 2 * 64 * 4
     assert L.s_entry == L.tp + slots * 8 * 64 * 16 * 2
     assert L.uc == L.s_entry + slots * 128 * 128 * 2
-    assert L.total == L.uc + slots * 128 * 64 * 2
-    assert B.gdn_prefill_scratch_bytes(2, 0, 4, 128, 128, B.gdn_varlen(P, P, 0, 0)) == 256
+    assert L.kfr == L.uc + slots * 128 * 64 * 2
+    assert L.total == L.kfr + chunks * 16 * 2 * 128 * 64 * 2
+    assert B.gdn_prefill_scratch_bytes(2, 0, 2, 4, 128, 128, B.gdn_varlen(P, P, 0, 0)) == 256
     # partial last chunk: T = 200 -> 4 chunks
-    assert B.gdn_prefill_scratch_layout(1, 200, 1, 128, 128).slots == 4
+    assert B.gdn_prefill_scratch_layout(1, 200, 1, 1, 128, 128).slots == 4
     # ragged: total_chunks decides
     vl = B.gdn_varlen(P, P, 2, 7)
-    assert B.gdn_prefill_scratch_layout(3, 0, 5, 128, 128, vl).slots == 35
-    assert B.gdn_prefill_scratch_bytes(1, 64, 1, 64, 128) == 0
+    assert B.gdn_prefill_scratch_layout(3, 0, 5, 5, 128, 128, vl).slots == 35
+    assert B.gdn_prefill_scratch_bytes(1, 64, 1, 1, 64, 128) == 0
+    assert B.gdn_prefill_scratch_bytes(1, 64, 3, 4, 128, 128) == 0
 
 
 def test_varlen_host_check():
