@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3]
 
-One step = one gdn_prefill call (all three stages) over the whole synthetic
-workload, inputs resident in HBM.  Default workload: B=4 sequences of T=8192
+One step = one gdn_prefill call (both kernels: stage 1, then the spine with the
+output fused in) over the whole synthetic workload, inputs resident in HBM.  Default workload: B=4 sequences of T=8192
 tokens, nk=16 k-heads, nv=32 v-heads, dk=dv=128, carried float32 state updated
 in place, per-chunk entry states emitted (the T=8192 workload the target is
 stated on).  Prints one JSON line.
@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN chunked prefill tokens/sec on 1 MI355X; % bf16 MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
-KERNELS = {1: "chunk_cumsum_recompute_wu", 2: "chunk_delta_h", 3: "chunk_fwd_o"}
-KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h.hip", 3: "k3_chunk_fwd_o.hip"}
+KERNELS = {1: "chunk_cumsum_recompute_wu", 2: "chunk_delta_h_fwd_o"}
+KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h_fwd_o.hip"}
 
 
 # ---------------------------------------------------------------------------
@@ -42,12 +42,13 @@ KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h.hip", 
 def algorithmic(p):
     """Per-kernel algorithmic bytes and flops for problem p (inputs.Problem).
 
-    Bytes: every operand each stage must read or write once (q, k counted once
-    per k-head).  Stage 1 reads k, g, beta and writes gc, the decays, T' (16
-    KB per chunk-head) and K, K^T fragments (32 KB per chunk and k-head); stage 2
-    reads T', the K fragments, v, the decays and the state and writes the entry states
-    (32 KB per chunk-head), uc (16 KB) and the state; stage 3 reads q, k, gc,
-    the decays, the entry states and uc and writes o.  Flops: dense-tile MFMA work per chunk-head."""
+    Bytes: every operand each kernel must read or write once (q, k counted once
+    per k-head).  Stage 1 reads k, g, beta and writes gc, the decays and T'
+    (12 KB per chunk-head); stage 2 reads q, k, v, gc, the decays, T' and the
+    state, and writes the entry states (32 KB per chunk-head), o and the state.
+    Flops: the dense-tile MFMA work per chunk-head of what each kernel computes
+    (Gram in stage 1; K h, T' R, K^T uc, Q h, the scores Q K^T and A uc in
+    stage 2), each product counted once."""
     N, nk, nv = p.n_tokens, p.nk, p.nv
     slots = int(p.cu_chunks[-1]) * nv
     nseq = p.nseq
@@ -58,22 +59,16 @@ def algorithmic(p):
     gb_bytes = N * nv * 8
     gc_bytes = slots * C * 4
     dec_bytes = slots * 2 * C * 4
-    tp_bytes = slots * C * C * 4
+    tp_bytes = slots * 2 * 6 * 64 * 16
     s_bytes = slots * d * d * 2
-    uc_bytes = slots * d * C * 2
     state_bytes = nseq * nv * d * d * 4
     o_bytes = N * nv * d * 2
-    kt_bytes = int(p.cu_chunks[-1]) * nk * C * d * 2 * 2   # K and K^T fragments, once per k-head
     by = {
-        1: k_bytes + gb_bytes + gc_bytes + dec_bytes + tp_bytes + kt_bytes,
-        2: tp_bytes + kt_bytes + v_bytes + dec_bytes + 2 * state_bytes + s_bytes + uc_bytes,
-        3: q_bytes + k_bytes + gc_bytes + dec_bytes // 2 + s_bytes + uc_bytes + o_bytes,
+        1: k_bytes + gb_bytes + gc_bytes + dec_bytes + tp_bytes,
+        2: q_bytes + k_bytes + v_bytes + gc_bytes + dec_bytes + tp_bytes + 2 * state_bytes + s_bytes + o_bytes,
     }
-    # Gram 2C^2 d; spine K h, T' R, K^T uc: 2Cd^2 + 2C^2 d + 2Cd^2; output
-    # Q S 2Cd^2, scores 2C^2 d, A uc 2C^2 d
     fl = {1: slots * (2 * C * C * d),
-          2: slots * (4 * C * d * d + 2 * C * C * d),
-          3: slots * (2 * C * d * d + 4 * C * C * d)}
+          2: slots * (6 * C * d * d + 6 * C * C * d)}
     return by, fl
 
 
@@ -102,30 +97,37 @@ def traffic_for(stage, workload_name):
 # is touched)
 
 
-def _oracle_chain(args):
-    idx, i, h, tmax, seconds = args
+def _oracle_worker(args):
+    w, workers, seconds = args
     from threadpoolctl import threadpool_limits
     from oracle import gdn_recurrence, kv_head_map
     from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64
     p = _SAMPLE_PROBLEM
-    a = int(p.cu_seqlens[i])
-    L = min(int(p.lengths[i]), tmax)
-    kap = kv_head_map(p.nk, p.nv)[[h]]
-    q = bf16_to_f64(p.q[a:a + L][:, kap])
-    k = bf16_to_f64(p.k[a:a + L][:, kap])
-    v = bf16_to_f64(p.v[a:a + L][:, [h]])
-    g = p.g[a:a + L][:, [h]].astype("float64")
-    b = p.beta[a:a + L][:, [h]].astype("float64")
-    h0 = p.h0[i][[h]].astype("float64")
+    kmap = kv_head_map(p.nk, p.nv)
     done = 0
     t0 = time.perf_counter()
     with threadpool_limits(1):
-        step = 256
-        while done < L and time.perf_counter() - t0 < seconds:
-            n = min(step, L - done)
-            _, h0, _ = gdn_recurrence(q[done:done + n], k[done:done + n], v[done:done + n],
-                                      g[done:done + n], b[done:done + n], h0)
-            done += n
+        # chains (sequence, v-head) in a fixed order, worker w takes every
+        # workers-th one, until its time is up
+        for chain in range(w, p.nseq * p.nv, workers):
+            i, h = chain % p.nseq, (chain // p.nseq * 7) % p.nv
+            a, L = int(p.cu_seqlens[i]), int(p.lengths[i])
+            kap = kmap[[h]]
+            q = bf16_to_f64(p.q[a:a + L][:, kap])
+            k = bf16_to_f64(p.k[a:a + L][:, kap])
+            v = bf16_to_f64(p.v[a:a + L][:, [h]])
+            g = p.g[a:a + L][:, [h]].astype("float64")
+            b = p.beta[a:a + L][:, [h]].astype("float64")
+            h0 = p.h0[i][[h]].astype("float64")
+            pos, step = 0, 256
+            while pos < L and time.perf_counter() - t0 < seconds:
+                n = min(step, L - pos)
+                _, h0, _ = gdn_recurrence(q[pos:pos + n], k[pos:pos + n], v[pos:pos + n],
+                                          g[pos:pos + n], b[pos:pos + n], h0)
+                pos += n
+                done += n
+            if time.perf_counter() - t0 >= seconds:
+                break
     return done, time.perf_counter() - t0
 
 
@@ -137,10 +139,10 @@ def cpu_baseline(p, seconds_per_worker=1.5):
     global _SAMPLE_PROBLEM
     _SAMPLE_PROBLEM = p
     workers = max(1, min(16, os.cpu_count() or 1))
-    jobs = [(w, w % p.nseq, (7 * w) % p.nv, 8192, seconds_per_worker) for w in range(workers)]
+    jobs = [(w, workers, seconds_per_worker) for w in range(workers)]
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(workers) as pool:
-        res = pool.map(_oracle_chain, jobs)
+        res = pool.map(_oracle_worker, jobs)
     wall = time.perf_counter() - t0
     token_heads = sum(r[0] for r in res)
     cpu_s = sum(r[1] for r in res)
@@ -149,9 +151,10 @@ def cpu_baseline(p, seconds_per_worker=1.5):
         "unit": "tokens/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": (f"{workers} (sequence, v-head) chains of this workload run through the float64 "
-                   f"token recurrence for ~{seconds_per_worker}s each ({token_heads} token-heads, "
-                   f"{cpu_s:.1f} core-s, wall {wall:.1f}s); tokens/s = token-heads/s / nv"),
+        "sample": (f"{workers} workers (one BLAS thread each) running (sequence, v-head) chains of this "
+                   f"workload through the float64 token recurrence for {seconds_per_worker}s each: "
+                   f"{token_heads} token-heads, {cpu_s:.1f} core-s, wall {wall:.1f}s; "
+                   f"tokens/s = token-heads/s / nv"),
     }
 
 
@@ -203,23 +206,21 @@ def main():
         dp.run()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    stages = sorted(KERNELS)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         e = ev[s]
         e[0].record()
-        dp.run_stage(1)
-        e[1].record()
-        dp.run_stage(2)
-        e[2].record()
-        dp.run_stage(3)
-        e[3].record()
+        for st in stages:
+            dp.run_stage(st)
+            e[st].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     per = {st: sum(ev[s][st - 1].elapsed_time(ev[s][st]) for s in range(args.steps)) / args.steps
-           for st in (1, 2, 3)}
+           for st in stages}
     ms_per_step = wall * 1e3 / args.steps
     tokens = p.n_tokens
     value = tokens / (ms_per_step / 1e3)
@@ -231,7 +232,7 @@ def main():
                              "alg_GBps": round(by[st] / (per[st] / 1e3) / 1e9, 1),
                              "hbm_frac": round(by[st] / (per[st] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                              "mfma_frac": round(fl[st] / (per[st] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-               for st in (1, 2, 3)}
+               for st in stages}
     total_bytes = sum(by.values())
     line = {
         "metric": METRIC,

@@ -8,16 +8,18 @@
  * (Gated DeltaNet, Yang, Kautz & Hatamizadeh, ICLR 2025).  It is evaluated in
  * 64-token chunks in the three stages the page
  * "spark_model/layers/ops/ssm_gdn_a3.rs" lists in the doc comment of
- * gdn_prefill_fla:
+ * gdn_prefill_fla, run as two kernels:
  *   1. chunk_cumsum_recompute_wu: chunk-local cumulative log-gate gc, the
  *      strictly lower L (sharing the key Gram), and the WY/UT solves
  *      (I+L) W = beta exp(gc) K, (I+L) U = beta V -- emitted as the UT
  *      transform T' = (I+L)^-1 diag(beta), which gives U = T' V and
  *      W = T' diag(exp(gc)) K;
- *   2. chunk_delta_h: a serial float32 state spine over chunks that emits each
- *      chunk's entry state and corrected values uc = U - W h
- *      (= T' (V - diag(exp(gc)) K h)), and leaves the final state in place;
- *   3. chunk_fwd_o: O = diag(exp(gc)) Q h_c + tril(decay * Q K^T) uc.
+ *   2. chunk_delta_h_fwd_o: the serial float32 state spine over chunks (the
+ *      page's chunk_delta_h), which emits each chunk's entry state, forms the
+ *      corrected values uc = U - W h (= T' (V - diag(exp(gc)) K h)), and leaves
+ *      the final state in place -- with the page's stage 3, chunk_fwd_o,
+ *      O = diag(exp(gc)) Q h_c + tril(decay * Q K^T) uc, formed in the same
+ *      pass while h_c and uc are still in registers.
  * The arguments follow that page's launcher (gdn_prefill_fla's parameter
  * list): separate k/v head counts, packed strided rows, optional ragged
  * cu_seqlens / cu_chunks, a per-request state pointer table, caller-owned
@@ -48,7 +50,7 @@
  * q, k, v, g, beta may alias each other (read-only).  out, scratch and the
  * state must not alias the inputs or each other.
  *
- * Execution.  gdn_prefill enqueues three kernels on `stream` (a hipStream_t)
+ * Execution.  gdn_prefill enqueues two kernels on `stream` (a hipStream_t)
  * and returns; there is no device synchronisation.  Asynchronous faults
  * surface at the caller's next synchronisation.  Calls on different streams
  * with disjoint outputs and scratch may run concurrently.
@@ -69,6 +71,9 @@ extern "C" {
 
 #define GDN_CHUNK 64
 #define GDN_HEAD_DIM 128
+/* Largest token-row pitch (qk_row, v_row, and nv*128 of out), in elements: the
+ * kernels address the 64 rows of a chunk with 32-bit byte offsets. */
+#define GDN_MAX_ROW_PITCH (1 << 24)
 
 enum {
   GDN_OK = 0,
@@ -80,8 +85,8 @@ enum {
 
 /* Token-row pitches in elements (the page's qk_stride, v_stride, gb_stride). */
 typedef struct gdn_strides {
-  int64_t qk_row; /* q and k rows (bf16 elements); multiple of 8 */
-  int64_t v_row;  /* v rows (bf16 elements); multiple of 8       */
+  int64_t qk_row; /* q and k rows (bf16 elements); multiple of 8, <= GDN_MAX_ROW_PITCH */
+  int64_t v_row;  /* v rows (bf16 elements); multiple of 8, <= GDN_MAX_ROW_PITCH       */
   int64_t gb_row; /* g and beta rows (float elements); >= nv     */
 } gdn_strides;
 
@@ -102,31 +107,25 @@ typedef struct gdn_varlen {
  *   gc      float [slots][64]        chunk-local cumulative log-gate G_t; rows
  *                                    past the sequence end repeat the last value
  *   dec     float [slots][2][64]     exp(G_t), then exp(G_{n-1} - G_t)
- *   tp      bf16  [slots][2][8][64][8] the UT transform T' = (I+L)^-1 diag(beta)
+ *   tp      bf16  [slots][2][6][64][8] the UT transform T' = (I+L)^-1 diag(beta)
  *                                    (so U = T' V, W = T' diag(exp(G)) K) as
  *                                    bf16 hi (index 0) and lo (index 1) parts
- *                                    in MFMA fragment order: fragment
- *                                    f = 2*mt + kb, lane l = 16q + r holds row
- *                                    t = 16mt + r, columns s = 32kb + 4q + e
- *                                    (e = 0..3) and s = 32kb + 16 + 4q + e
+ *                                    in MFMA fragment order.  Of the 16x32
+ *                                    fragments (mt, kb) (rows 16mt.., columns
+ *                                    32kb..) only the lower-triangular six,
+ *                                    mt >= 2kb, are stored, at f = mt for kb = 0
+ *                                    and f = mt + 2 for kb = 1; lane l = 16q + r
+ *                                    of fragment f holds row t = 16mt + r,
+ *                                    columns s = 32kb + 4q + e (e = 0..3) and
+ *                                    s = 32kb + 16 + 4q + e
  *   s_entry bf16  [slots][128][128]  entry state of each chunk as S = h^T
  *                                    ([dv][dk], the recurrence's orientation);
  *                                    dense input: [B][nv][T/64][dv][dk]
- *   uc      bf16  [slots][128][64]   corrected values uc = U - W h, stored
- *                                    transposed ([dv][token])
- *   kfr     bf16  [kslots][2][16][64][8] K of each (sequence, k-head, chunk)
- *                                    in two MFMA fragment orders; kslot(i, kh, c)
- *                                    = cu_chunks[i]*nk + kh*n_i + c.  Index 0,
- *                                    fragment f = 4*mt + kb, lane 16q + r:
- *                                    K[16mt + r][32kb + 4q + e] and
- *                                    K[16mt + r][32kb + 16 + 4q + e]; index 1,
- *                                    fragment f = 2*m + kb: K[32kb + 4q + e][16m + r]
- *                                    and K[32kb + 16 + 4q + e][16m + r] (e = 0..3)
  */
 typedef struct gdn_scratch_layout {
-  size_t gc, dec, tp, s_entry, uc, kfr; /* byte offsets */
-  size_t total;                    /* bytes needed */
-  int64_t slots;                   /* chunk slots  */
+  size_t gc, dec, tp, s_entry; /* byte offsets */
+  size_t total;                /* bytes needed */
+  int64_t slots;               /* chunk slots  */
 } gdn_scratch_layout;
 
 /* Scratch bytes for a problem (at least 256).  varlen NULL: dense B x T.
@@ -174,10 +173,9 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
                 const gdn_strides *strides, const gdn_varlen *varlen, void *stream);
 
 /*
- * One stage of gdn_prefill (1, 2 or 3), same arguments, same validation.
- * Stage s reads what stage s-1 left in scratch; running 1, 2, 3 in order on
- * one stream is exactly gdn_prefill.  For callers that time or interleave the
- * stages.
+ * One kernel of gdn_prefill (stage 1 or 2), same arguments, same validation.
+ * Stage 2 reads what stage 1 left in scratch; running 1 then 2 on one stream
+ * is exactly gdn_prefill.  For callers that time or interleave the kernels.
  */
 int gdn_prefill_stage(int stage, const void *q, const void *k, const void *v, const float *g,
                       const float *beta, void *h_state, int h_state_is_table, void *out,

@@ -34,8 +34,7 @@ class gdn_varlen(ctypes.Structure):
 
 class gdn_scratch_layout(ctypes.Structure):
     _fields_ = [("gc", ctypes.c_size_t), ("dec", ctypes.c_size_t), ("tp", ctypes.c_size_t),
-                ("s_entry", ctypes.c_size_t), ("uc", ctypes.c_size_t), ("kfr", ctypes.c_size_t),
-                ("total", ctypes.c_size_t),
+                ("s_entry", ctypes.c_size_t), ("total", ctypes.c_size_t),
                 ("slots", ctypes.c_int64)]
 
 

@@ -1,6 +1,6 @@
 // gdn_api.hip -- the C ABI of include/gdn_prefill.h: argument validation
-// (pure host logic), the scratch layout, and the three launches on the
-// caller's stream.
+// (pure host logic), the scratch layout, and the two launches on the caller's
+// stream.
 //
 // Convention from the page "spark_model/layers/ops/ssm_gdn_a3.rs"
 // (gdn_tc_spine_reject): every rejection names the guard that rejected, and a
@@ -17,7 +17,6 @@
 namespace gdn {
 hipError_t launch_stage1(const Params &p, hipStream_t stream);
 hipError_t launch_stage2(const Params &p, hipStream_t stream);
-hipError_t launch_stage3(const Params &p, hipStream_t stream);
 } // namespace gdn
 
 namespace {
@@ -72,10 +71,6 @@ int layout(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varle
   off = align256(off + size_t(slots) * gdn::kTpBytes);
   out->s_entry = off;
   off = align256(off + size_t(slots) * gdn::kSBytes);
-  out->uc = off;
-  off = align256(off + size_t(slots) * gdn::kUcBytes);
-  out->kfr = off;
-  off = align256(off + size_t(chunks) * nk * gdn::kKfrBytes);
   out->total = off > 256 ? off : 256; // never 0 for a valid problem
   return ok();
 }
@@ -119,6 +114,11 @@ int validate(const void *q, const void *k, const void *v, const float *g, const 
   if (strides->v_row < int64_t(nv) * GDN_HEAD_DIM)
     return fail(GDN_EINVAL, "strides: v_row=%lld is smaller than nv*128=%d", (long long)strides->v_row,
                 nv * GDN_HEAD_DIM);
+  if (strides->qk_row > GDN_MAX_ROW_PITCH || strides->v_row > GDN_MAX_ROW_PITCH)
+    return fail(GDN_EINVAL, "strides: qk_row=%lld and v_row=%lld must not exceed %d elements",
+                (long long)strides->qk_row, (long long)strides->v_row, GDN_MAX_ROW_PITCH);
+  if (int64_t(nv) * GDN_HEAD_DIM > GDN_MAX_ROW_PITCH)
+    return fail(GDN_EINVAL, "head counts: nv=%d makes output rows longer than %d elements", nv, GDN_MAX_ROW_PITCH);
   if (strides->gb_row < nv)
     return fail(GDN_EINVAL, "strides: gb_row=%lld is smaller than nv=%d", (long long)strides->gb_row, nv);
   if (varlen) {
@@ -160,8 +160,6 @@ gdn::Params make_params(const void *q, const void *k, const void *v, const float
   p.dec = reinterpret_cast<float *>(base + lay.dec);
   p.tp = reinterpret_cast<uint16_t *>(base + lay.tp);
   p.s_entry = reinterpret_cast<uint16_t *>(base + lay.s_entry);
-  p.uc = reinterpret_cast<uint16_t *>(base + lay.uc);
-  p.kfr = reinterpret_cast<uint16_t *>(base + lay.kfr);
   p.qk_row = strides->qk_row;
   p.v_row = strides->v_row;
   p.gb_row = strides->gb_row;
@@ -186,12 +184,9 @@ gdn::Params make_params(const void *q, const void *k, const void *v, const float
 }
 
 int run_stage(int stage, const gdn::Params &p, hipStream_t stream) {
-  static const char *names[4] = {"", "chunk_cumsum_recompute_wu", "chunk_delta_h", "chunk_fwd_o"};
+  static const char *names[3] = {"", "chunk_cumsum_recompute_wu", "chunk_delta_h_fwd_o"};
   if (p.max_chunks == 0) return ok(); // every sequence is empty: nothing to do
-  hipError_t e = hipSuccess;
-  if (stage == 1) e = gdn::launch_stage1(p, stream);
-  else if (stage == 2) e = gdn::launch_stage2(p, stream);
-  else e = gdn::launch_stage3(p, stream);
+  const hipError_t e = (stage == 1) ? gdn::launch_stage1(p, stream) : gdn::launch_stage2(p, stream);
   if (e != hipSuccess)
     return fail(GDN_EHIP, "launch of %s failed: %s", names[stage], hipGetErrorString(e));
   return ok();
@@ -226,7 +221,7 @@ int gdn_prefill_stage(int stage, const void *q, const void *k, const void *v, co
                       const float *beta, void *h_state, int h_state_is_table, void *out, void *scratch,
                       size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
                       const gdn_strides *strides, const gdn_varlen *varlen, void *stream) {
-  if (stage < 1 || stage > 3) return fail(GDN_EINVAL, "stage=%d must be 1, 2 or 3", stage);
+  if (stage < 1 || stage > 2) return fail(GDN_EINVAL, "stage=%d must be 1 or 2", stage);
   gdn_scratch_layout lay;
   int rc = validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk,
                     nv, dk, dv, strides, varlen, &lay);
@@ -246,7 +241,7 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
   if (rc != GDN_OK) return rc;
   const gdn::Params p = make_params(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, B, T, nk,
                                     nv, strides, varlen, lay);
-  for (int stage = 1; stage <= 3; ++stage) {
+  for (int stage = 1; stage <= 2; ++stage) {
     rc = run_stage(stage, p, static_cast<hipStream_t>(stream));
     if (rc != GDN_OK) return rc;
   }

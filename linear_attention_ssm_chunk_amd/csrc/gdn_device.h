@@ -110,6 +110,30 @@ __device__ __forceinline__ bf16x8 ident_chain(int lane, int half) {
   return f;
 }
 
+// The dk order of the spine.  Row rho = 16m + 4q + i of the state tiles
+// (m = 0..7, q, i = 0..3) holds dk = perm_dk(rho) = 32(m/2) + 8q + 4(m%2) + i.
+// Then the chain fragment of tiles (2kb, 2kb+1) gives a lane eight consecutive
+// dk, 32kb + 8q .. +7: K and Q rows are read, and entry states written, as
+// 16-byte pieces, and the contiguous k order of a row fragment is this order.
+__host__ __device__ constexpr int perm_dk(int rho) {
+  return 32 * (rho >> 5) + 8 * ((rho >> 2) & 3) + 4 * ((rho >> 4) & 1) + (rho & 3);
+}
+
+// B operand that turns a row fragment (contiguous k order) into the columns
+// perm_dk(16*half + j), j = 0..15, of its 32-wide k block: the product's C
+// tile holds, at column j, the row element of dk perm_dk(16*half + j).
+__device__ __forceinline__ bf16x8 ident_perm(int lane, int half) {
+  const int q = lane >> 4, j = lane & 15;
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = to_bf16((8 * q + e == perm_dk(16 * half + j)) ? 1.f : 0.f);
+  return f;
+}
+
+// Fragment slot of a lower-triangular 64x64 A operand (T', the scores) held as
+// 16x32 fragments (mt, kb): only mt >= 2kb can be nonzero, six in all.
+__host__ __device__ constexpr int tri_frag(int mt, int kb) { return kb == 0 ? mt : mt + 2; }
+
 __device__ __forceinline__ bf16x8 load16_bf16x8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }

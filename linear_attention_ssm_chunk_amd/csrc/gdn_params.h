@@ -1,4 +1,4 @@
-// gdn_params.h -- one parameter block shared by the host launcher and the three
+// gdn_params.h -- one parameter block shared by the host launcher and the two
 // kernels, so the two sides cannot disagree about sizes or layouts (the page
 // "spark_model/layers/ops/ssm_gdn_a3.rs" makes the same point about its
 // shared-memory footprint constant GDN_TC_SMEM).
@@ -10,15 +10,13 @@ namespace gdn {
 
 constexpr int kChunk = 64;    // tokens per chunk
 constexpr int kDim = 128;     // dk = dv
-constexpr int kThreads = 256; // every kernel: 4 waves of 64
 
 // Bytes per chunk slot of each scratch region (see include/gdn_prefill.h).
-constexpr int64_t kGcBytes = int64_t(kChunk) * 4;       // G_t
-constexpr int64_t kDecBytes = int64_t(2) * kChunk * 4;  // exp(G_t), exp(G_{n-1} - G_t)
-constexpr int64_t kTpBytes = int64_t(8) * 64 * 16 * 2;  // T' hi/lo fragments (16 KB)
-constexpr int64_t kSBytes = int64_t(kDim) * kDim * 2;   // entry state, bf16 [dv][dk]
-constexpr int64_t kUcBytes = int64_t(kDim) * kChunk * 2; // uc, bf16 [dv][t]
-constexpr int64_t kKfrBytes = int64_t(2) * kDim * kChunk * 2; // K and K^T fragments, per k-head
+constexpr int kTpFrags = 6;                              // nonzero 16x32 fragments of T' (lower triangle)
+constexpr int64_t kGcBytes = int64_t(kChunk) * 4;        // G_t
+constexpr int64_t kDecBytes = int64_t(2) * kChunk * 4;   // exp(G_t), exp(G_{n-1} - G_t)
+constexpr int64_t kTpBytes = int64_t(2) * kTpFrags * 64 * 16; // T' hi/lo fragments (12 KB)
+constexpr int64_t kSBytes = int64_t(kDim) * kDim * 2;    // entry state, bf16 [dv][dk]
 
 struct Params {
   // inputs (bf16 as raw 16-bit patterns)
@@ -30,7 +28,7 @@ struct Params {
   uint16_t *out; // bf16 [N_tok][nv][dv]
   // scratch regions
   float *gc, *dec;
-  uint16_t *tp, *s_entry, *uc, *kfr;
+  uint16_t *tp, *s_entry;
   int64_t qk_row, v_row, gb_row; // token-row pitches in elements
   int B, T, nk, nv;
   int n_chunks;                  // dense: ceil(T/64)

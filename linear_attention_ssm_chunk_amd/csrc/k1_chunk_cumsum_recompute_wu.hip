@@ -9,9 +9,8 @@
 //   L[r,s] = beta_r exp(G_r - G_s) (k_r . k_s)        (s < r, else 0)
 //   T'     = (I + L)^-1 diag(beta)                     (the UT transform)
 // so that U = T' V and W = T' diag(exp(G)) K.  This stage emits T' itself
-// (16 KB per chunk-head) instead of W and U (64 KB in float32): the spine forms
-// uc = U - W h = T' (V - diag(exp(G)) K h) on the fly, which moves a third of
-// the bytes the three stages would otherwise move.
+// (12 KB per chunk-head) instead of W and U (64 KB in float32): the spine forms
+// uc = U - W h = T' (V - diag(exp(G)) K h) on the fly from T', K and V.
 //
 // One wave per (chunk, v-head):
 //   * lane t scans g; emits gc, exp(G_t) and exp(G_{n-1} - G_t);
@@ -22,9 +21,8 @@
 //   * the off-diagonal block T21 = -T22 (L21 T11) on MFMA, every operand split
 //     into bf16 hi + lo (three products each, ~2^-17 relative error);
 //   * T' = T diag(beta), split hi/lo, stored in the exact A-operand fragment
-//     order the spine reads (hi and lo: 8 fragments x 64 lanes x 16 bytes each);
-//   * once per k-head, K and K^T in the spine's A-operand fragment orders
-//     (2 x 16 KB), so the serial spine never transposes or permutes.
+//     order the spine reads (hi and lo: the 6 nonzero fragments x 64 lanes x
+//     16 bytes each).
 #include "gdn_device.h"
 
 namespace gdn {
@@ -181,41 +179,16 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
     }
   }
 
-  // ---- K in the spine's two A-operand orders (one v-head per k-head writes
-  // them): kfr[0] fragment (mt, kb) holds rows t = 16mt + r16, columns
-  // dk = 32kb + {4q..4q+3, 16+4q..16+4q+3} (for K h); kfr[1] fragment (m, kb)
-  // holds rows dk = 16m + r16, tokens t = 32kb + {4q.., 16+4q..} (for K^T uc),
-  // the transpose being an identity product on K's own rows. --------------
-  if (h % (p.nv / p.nk) == 0) {
-    u32x4 *kfr = reinterpret_cast<u32x4 *>(p.kfr + (s.chunk0 * p.nk + int64_t(kh) * s.nchunks + c) * (2 * 16 * 64 * 8));
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int t = 16 * mt + r16;
-      const uint16_t *kr = kbase + int64_t(t) * p.qk_row + 4 * q4;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kfr[(mt * 4 + kb) * 64 + lane] = (t < n) ? __builtin_bit_cast(u32x4, join8(load8(kr + 32 * kb), load8(kr + 32 * kb + 16)))
-                                                 : u32x4{0u, 0u, 0u, 0u};
-    }
-    const bf16x8 I0 = ident_contig(lane, 0), I1 = ident_contig(lane, 1);
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f32x4 d0 = mfma(kf[2 * kb][m >> 1], (m & 1) ? I1 : I0, zero4());
-        const f32x4 d1 = mfma(kf[2 * kb + 1][m >> 1], (m & 1) ? I1 : I0, zero4());
-        kfr[16 * 64 + (m * 2 + kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(d0, d1));
-      }
-  }
-
   // ---- T' = T diag(beta) in the spine's A-operand order: fragment (mt, kb)
   // holds rows t = 16mt + r16, columns s = 32kb + {4q..4q+3, 16+4q..16+4q+3};
-  // the 8 hi fragments, then the 8 lo fragments, 16 bytes per lane ----------
-  uint16_t *tp = p.tp + slot * (8 * 64 * 16);
+  // only the six with mt >= 2kb are stored (T' is lower triangular): the hi
+  // parts, then the lo parts, 16 bytes per lane ------------------------------
+  u32x4 *dst = reinterpret_cast<u32x4 *>(p.tp + slot * (kTpBytes / 2));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      if (2 * kb > mt) continue;
       const int t = 16 * mt + r16;
       const int s0 = 32 * kb + 4 * q4, s1 = s0 + 16;
       const f32x4 a = *reinterpret_cast<const f32x4 *>(Ls + t * kLP + s0);
@@ -224,9 +197,8 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
                           b[0] * Bs[s1], b[1] * Bs[s1 + 1], b[2] * Bs[s1 + 2], b[3] * Bs[s1 + 3]};
       bf16x8 hi, lo;
       split8(x, hi, lo);
-      u32x4 *dst = reinterpret_cast<u32x4 *>(tp);
-      dst[(mt * 2 + kb) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
-      dst[8 * 64 + (mt * 2 + kb) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
+      dst[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
+      dst[(kTpFrags + tri_frag(mt, kb)) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
     }
 }
 

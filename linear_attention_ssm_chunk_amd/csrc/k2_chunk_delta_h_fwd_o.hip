@@ -1,0 +1,462 @@
+// Stage 2: chunk_delta_h with the chunk output (chunk_fwd_o) fused in.
+//
+// Page "spark_model/layers/ops/ssm_gdn_a3.rs", doc comment of gdn_prefill_fla,
+// stages 2 and 3: a serial pass over the chunks of each (sequence, v-head) that
+// emits the per-chunk entry states, updates h_state in place, and forms each
+// chunk's output.  Per chunk, with h the entry state (stored [dk][dv], float32)
+// and T' the UT transform from stage 1:
+//   S_entry[c] = bf16(h^T)                                  ([dv][dk])
+//   uc         = U - W h = T' (V - diag(exp(G)) K h)
+//   O          = diag(exp(G)) Q h + A uc,  A = tril_incl(exp(G_t - G_s) q_t.k_s)
+//   h         <- exp(G_n) h + K^T diag(exp(G_n - G)) uc     (G_n: last token)
+// Stage 3 of the page reads the entry state and uc back from memory; here both
+// are still in registers when the output is formed, so neither uc nor a second
+// read of the entry state ever reaches HBM.
+//
+// The dv columns of h evolve independently, so the state is split into
+// 16-column strips (the page's DV-block split, tc_vblock comment).  A
+// workgroup covers S strips of one chain (S = 1, 2 or 4, chosen so the grid
+// fills the chip: few long chains get more workgroups each):
+//   * waves 0..S-1 (compute): one strip each for the whole pass.  The strip
+//     lives in MFMA accumulators; in the chain k order those registers are the
+//     B operand of K h and Q h directly, and so are the C tiles of
+//     R = V - e^G K h (for T' R) and of uc (for K^T uc and A uc): the
+//     dependent chain never leaves registers;
+//   * waves S..S+3 (loaders), two pairs; the pair that owns chunk c+1 stages
+//     it into the free half of a double-buffered LDS stage, from registers it
+//     filled two steps earlier, then fetches chunk c+3:
+//       - wave 0 of the pair: Q and K as whole rows (1 KB per load), written
+//         to LDS row tiles; from the row fragments it reads back, the causal
+//         decayed scores A and K^T (identity products) on MFMA;
+//       - wave 1 of the pair: the T' fragments, the decays, and V turned by
+//         identity products into the compute waves' C-tile order.
+// One barrier per chunk.  Entry states leave as 16-byte pieces (dk order
+// perm_dk); outputs as 8-byte pieces of whole token rows after an identity
+// product.
+// Precision: h is float32 between chunks; h, R and the decayed uc are split
+// into bf16 hi+lo for the products that feed the state (K is exact in bf16, T'
+// arrives split), so every product keeps ~2^-17 relative error with bf16 MFMA
+// and float32 accumulation.  The output uses bf16(h) and bf16(uc) -- the
+// page's stage 3 reads both in bf16 -- with float32 accumulation.
+//
+// Workgroup order: all workgroups that read one k-head's rows (its r v-heads
+// x column groups) get the same blockIdx.x % 8, so that on a round-robin XCD
+// dispatch they share one XCD's L2.
+#include "gdn_device.h"
+
+namespace gdn {
+
+// Q and K tiles are kept as rows (64 rows of 16 pieces of 16 bytes), piece p of
+// row t at slot 16t + (p ^ (t % 16)): a whole row is written by 16 lanes at
+// once, and a row fragment (16 rows, one piece each) is read, without bank
+// conflicts.
+__device__ __forceinline__ int row_slot(int t, int piece) { return 16 * t + (piece ^ (t & 15)); }
+
+struct Stage {
+  u32x4 kr[64 * 16];          // K rows: A operand of K h (fragment (mt, kb): rows 16mt + r16, piece 4kb + q)
+  u32x4 qr[64 * 16];          // Q rows: A operand of Q h
+  u32x4 kt[16 * 64];          // K^T, A operand of K^T uc: fragment 2m + kb (rows in perm_dk order)
+  u32x4 tp[2 * kTpFrags * 64]; // T' fragments: 6 hi, then 6 lo
+  u32x4 af[kTpFrags * 64];    // scores A, A operand of A uc: fragment tri_frag(mt, kb)
+  u32x2 vt[4 * 4 * 64];       // V in C-tile order: (strip, mt), lane -> 4 rows of its column
+  float dec[2 * kChunk];      // exp(G_t), exp(G_{n-1} - G_t)
+};
+
+// Split two C tiles (a k block of 32 rows, chain order) into hi / lo bf16
+// fragments.  hi = bf16(x); x - hi is exact in float32 and comes from one bf16
+// dot product per element, (hi0, hi1) . (-1, 0) + x0, with the constant pairs
+// in registers m0, m1 (an inline constant would be read as the float32 -1.0).
+__device__ __forceinline__ void split_tiles(const f32x4 &t0, const f32x4 &t1, uint32_t m0, uint32_t m1, bf16x8 &hi,
+                                            bf16x8 &lo) {
+  uint32_t h[4], l[4];
+  float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = cvt_pk(x[2 * e], x[2 * e + 1]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 h2 = __builtin_bit_cast(bf16x2, h[e]);
+    x[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(h2, __builtin_bit_cast(bf16x2, m0), x[2 * e], false);
+    x[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(h2, __builtin_bit_cast(bf16x2, m1), x[2 * e + 1], false);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) l[e] = cvt_pk(x[2 * e], x[2 * e + 1]);
+  hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+template <int kStrips>
+__global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params p) {
+  constexpr int kGroups = 8 / kStrips; // workgroups per chain
+  // ---- which (sequence, v-head, column group) ----------------------------
+  const int r = p.nv / p.nk;
+  const int b = blockIdx.x;
+  const int idx = b >> 3;
+  const int kgroup = (b & 7) + 8 * (idx / (r * kGroups)); // (sequence, k-head)
+  if (kgroup >= p.B * p.nk) return;
+  const int j = (idx / kGroups) % r, cg = idx % kGroups;
+  const int i = kgroup / p.nk, kh = kgroup % p.nk;
+  const int h = kh * r + j;
+  const Seq s = seq_of(p, i);
+  if (!s.ok || s.nchunks == 0) return; // length 0: the state is left as it is
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int col0 = cg * 16 * kStrips; // first column of this workgroup
+
+  __shared__ Stage st[2];
+
+  // =========================== loader waves ===============================
+  if (wave >= kStrips) {
+    const int pair = (wave - kStrips) >> 1; // owns chunks c with c % 2 == pair
+    const int role = (wave - kStrips) & 1;
+    const int nrow = lane >> 4, piece = lane & 15; // whole-row loads: 4 rows per instruction
+
+    if (role == 0) {
+      // ---- Q, K rows; the scores and K^T from them --------------------------
+      u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
+      float gt[4];          // G at t = 16mt + r16
+      f32x4 gs[4];          // G at s = 16ms + 4q .. +3
+      auto fetch = [&](int c) {
+        const int nn = min(kChunk, s.len - c * kChunk);
+        // chunk bases are wave-uniform; a lane adds a 32-bit offset (row
+        // pitches are bounded so that 64 rows stay below 2^31 bytes)
+        const int64_t row0 = (s.tok0 + int64_t(c) * kChunk) * p.qk_row + int64_t(kh) * kDim;
+        const char *qc = reinterpret_cast<const char *>(p.q + row0);
+        const char *kc = reinterpret_cast<const char *>(p.k + row0);
+        const uint32_t pitch = uint32_t(p.qk_row) * 2u;
+#pragma unroll
+        for (int jr = 0; jr < 16; ++jr) {
+          // rows past the sequence end repeat its last row: they only reach
+          // rows of products that are never stored, or meet zero rows of T'
+          const uint32_t off = uint32_t(min(4 * jr + nrow, nn - 1)) * pitch + 16u * piece;
+          qx[jr] = *reinterpret_cast<const u32x4 *>(qc + off);
+          kx[jr] = *reinterpret_cast<const u32x4 *>(kc + off);
+        }
+        const float *gc = p.gc + slot_of(p, s, h, c) * kChunk;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          gt[m] = gc[16 * m + r16];
+          gs[m] = *reinterpret_cast<const f32x4 *>(gc + 16 * m + 4 * q4);
+        }
+      };
+      const bf16x8 P0 = ident_perm(lane, 0), P1 = ident_perm(lane, 1);
+      auto stash = [&](Stage &S) {
+#pragma unroll
+        for (int jr = 0; jr < 16; ++jr) {
+          S.qr[row_slot(4 * jr + nrow, piece)] = qx[jr];
+          S.kr[row_slot(4 * jr + nrow, piece)] = kx[jr];
+        }
+        // Row fragments are read back from the tiles this wave just wrote, a
+        // few at a time: frag(T, mt, kb) = rows 16mt + r16, columns 32kb + 8q .. +7.
+        auto frag = [&](const u32x4 *T, int mt, int kb) {
+          return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
+        };
+        // C(ms, mt)[s][t] = q_t . k_s: A = K rows s, B = Q rows t; lane holds
+        // column t = 16mt + r16, rows s = 16ms + 4q .. +3.  Masked to s <= t and
+        // decayed by exp(G_t - G_s), two vertically stacked tiles are the
+        // chain-order A fragment (mt, kb) of A uc.
+        constexpr float kLog2e = 1.4426950408889634f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int t = 16 * mt + r16;
+          const float g2t = gt[mt] * kLog2e;
+          bf16x8 qf[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) qf[kk] = frag(S.qr, mt, kk);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            if (2 * kb > mt) continue;
+            f32x4 sc[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const int ms = 2 * kb + hf;
+              f32x4 acc = zero4();
+              if (ms <= mt) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mfma(frag(S.kr, ms, kk), qf[kk], acc);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                  const int si = 16 * ms + 4 * q4 + ii;
+                  acc[ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - gs[ms][ii] * kLog2e) * acc[ii] : 0.f;
+                }
+              }
+              sc[hf] = acc;
+            }
+            S.af[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[0], sc[1]));
+          }
+        }
+        // K^T fragment (m, kb): rows dk = perm_dk(16m + r16), tokens 32kb +
+        // chain order: the C tiles of row fragments (2kb, m/2) and (2kb+1, m/2)
+        // times the column picker of half m % 2.
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 f0 = frag(S.kr, 2 * kb, kd), f1 = frag(S.kr, 2 * kb + 1, kd);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const f32x4 c0 = mfma(f0, hf ? P1 : P0, zero4());
+              const f32x4 c1 = mfma(f1, hf ? P1 : P0, zero4());
+              S.kt[(2 * (2 * kd + hf) + kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(c0, c1));
+            }
+          }
+      };
+      if (pair < s.nchunks) fetch(pair);
+      if (pair == 0) {
+        stash(st[0]);
+        if (2 < s.nchunks) fetch(2);
+      }
+      __syncthreads();
+      for (int c = 0; c < s.nchunks; ++c) {
+        if (((c + 1) & 1) == pair && c + 1 < s.nchunks) {
+          stash(st[(c + 1) & 1]);
+          if (c + 3 < s.nchunks) fetch(c + 3);
+        }
+        __syncthreads();
+      }
+      return;
+    }
+
+    // ---- T', decays, V -----------------------------------------------------
+    u32x4 tx[2 * kTpFrags];
+    float d0 = 0.f, d1 = 0.f;
+    // V fragments: vx[mt][blk] = V[16mt + r16][col0 + 32blk + 8q .. +7]
+    constexpr int kBlk = (kStrips + 1) / 2; // 32-column blocks (a 1-strip group reads 32, uses 16)
+    u32x4 vx[4][kBlk];
+    const int vcol = (kStrips == 1 ? (col0 & ~31) : col0) + 8 * q4; // lane's first column
+    auto fetch = [&](int c) {
+      const int64_t sl = slot_of(p, s, h, c);
+      const u32x4 *tsrc = reinterpret_cast<const u32x4 *>(p.tp + sl * (kTpBytes / 2));
+#pragma unroll
+      for (int f = 0; f < 2 * kTpFrags; ++f) tx[f] = tsrc[f * 64 + lane];
+      d0 = p.dec[sl * 2 * kChunk + lane];
+      d1 = p.dec[sl * 2 * kChunk + kChunk + lane];
+      const int nn = min(kChunk, s.len - c * kChunk);
+      const char *vc = reinterpret_cast<const char *>(p.v + (s.tok0 + int64_t(c) * kChunk) * p.v_row + int64_t(h) * kDim);
+      const uint32_t pitch = uint32_t(p.v_row) * 2u;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t off = uint32_t(min(16 * mt + r16, nn - 1)) * pitch + 2u * vcol;
+#pragma unroll
+        for (int bk = 0; bk < kBlk; ++bk) vx[mt][bk] = *reinterpret_cast<const u32x4 *>(vc + off + 64u * bk);
+      }
+    };
+    const bf16x8 I0 = ident_contig(lane, 0), I1 = ident_contig(lane, 1);
+    auto stash = [&](Stage &S) {
+#pragma unroll
+      for (int f = 0; f < 2 * kTpFrags; ++f) S.tp[f * 64 + lane] = tx[f];
+      S.dec[lane] = d0;
+      S.dec[kChunk + lane] = d1;
+      // V tile (strip w, mt): lane (q, r16) gets V[16mt + 4q .. +3][strip column r16]
+#pragma unroll
+      for (int w = 0; w < kStrips; ++w) {
+        const int cw = (kStrips == 1 ? (col0 & 31) : 16 * w); // strip offset in the fetched block
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 c0 = mfma(__builtin_bit_cast(bf16x8, vx[mt][cw >> 5]), ((cw >> 4) & 1) ? I1 : I0, zero4());
+          S.vt[(w * 4 + mt) * 64 + lane] = pack4_bf16(c0[0], c0[1], c0[2], c0[3]);
+        }
+      }
+    };
+    if (pair < s.nchunks) fetch(pair);
+    if (pair == 0) {
+      stash(st[0]);
+      if (2 < s.nchunks) fetch(2);
+    }
+    __syncthreads();
+    for (int c = 0; c < s.nchunks; ++c) {
+      if (((c + 1) & 1) == pair && c + 1 < s.nchunks) {
+        stash(st[(c + 1) & 1]);
+        if (c + 3 < s.nchunks) fetch(c + 3);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // =========================== compute waves ==============================
+  const int colw = col0 + 16 * wave; // this wave's strip
+  float *hp = state_of(p, i, h);
+  f32x4 H[8]; // H[m][ii] = h[perm_dk(16m + 4q + ii)][colw + r16]
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) H[m][ii] = hp[perm_dk(16 * m + 4 * q4 + ii) * kDim + colw + r16];
+
+  // bf16 pairs (-1, 0) and (0, -1) for split_tiles, kept in registers
+  uint32_t m0 = 0x0000BF80u, m1 = 0xBF800000u;
+  asm volatile("" : "+v"(m0));
+  asm volatile("" : "+v"(m1));
+  const bf16x8 C0 = ident_chain(lane, 0), C1 = ident_chain(lane, 1);
+  const int64_t orow = int64_t(p.nv) * kDim;
+
+  __syncthreads(); // chunk 0 staged
+
+  for (int c = 0; c < s.nchunks; ++c) {
+    const Stage &S = st[c & 1];
+    const int64_t sl = slot_of(p, s, h, c);
+    const int n = min(kChunk, s.len - c * kChunk);
+
+    // h -> hi/lo bf16, chain order over dk (a lane's eight values are dk
+    // 32kb + 8q .. +7); bf16(h) is also the entry state
+    bf16x8 Hh[4], Hl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) split_tiles(H[2 * kb], H[2 * kb + 1], m0, m1, Hh[kb], Hl[kb]);
+    {
+      // S_c = h^T: row dv = colw + r16, dk = 32kb + 8q .. +7
+      uint16_t *sdst = p.s_entry + sl * (kDim * kDim) + (colw + r16) * kDim + 8 * q4;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<u32x4 *>(sdst + 32 * kb) = __builtin_bit_cast(u32x4, Hh[kb]);
+    }
+
+    // K h  (C tile mt: column colw + r16, rows t = 16mt + 4q .. +3)
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 ka[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) ka[mt] = __builtin_bit_cast(bf16x8, S.kr[row_slot(16 * mt + r16, 4 * kb + q4)]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[mt], Hh[kb], acc[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[mt], Hl[kb], acc[mt]);
+    }
+    // Q h (bf16 h): the state term of the output
+    f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 qa[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) qa[mt] = __builtin_bit_cast(bf16x8, S.qr[row_slot(16 * mt + r16, 4 * kb + q4)]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(qa[mt], Hh[kb], O[mt]);
+    }
+
+    // R = V - diag(exp(G)) K h
+    f32x4 eg[4];
+    f32x4 R[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      eg[mt] = *reinterpret_cast<const f32x4 *>(S.dec + 16 * mt + 4 * q4);
+      const u32x2 vv = S.vt[(wave * 4 + mt) * 64 + lane];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const uint32_t pr = vv[ii >> 1];
+        const float v = __builtin_bit_cast(float, (ii & 1) ? (pr & 0xFFFF0000u) : (pr << 16));
+        R[mt][ii] = v - eg[mt][ii] * acc[mt][ii];
+      }
+    }
+    bf16x8 Rh[2], Rl[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) split_tiles(R[2 * kb], R[2 * kb + 1], m0, m1, Rh[kb], Rl[kb]);
+
+    // uc = T' R  (T' is lower triangular: fragment (mt, 1) is zero for mt < 2)
+    f32x4 D[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 th[4], tl[4];
+#pragma unroll
+      for (int mt = 2 * kb; mt < 4; ++mt) {
+        th[mt] = __builtin_bit_cast(bf16x8, S.tp[tri_frag(mt, kb) * 64 + lane]);
+        tl[mt] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + tri_frag(mt, kb)) * 64 + lane]);
+      }
+#pragma unroll
+      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[mt], Rh[kb], D[mt]);
+#pragma unroll
+      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[mt], Rl[kb], D[mt]);
+#pragma unroll
+      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(tl[mt], Rh[kb], D[mt]);
+    }
+
+    // O = diag(exp(G)) Q h + A bf16(uc)
+    bf16x8 ub[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) ub[kb] = chain_frag(D[2 * kb], D[2 * kb + 1]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) O[mt] *= eg[mt];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int mt = 2 * kb; mt < 4; ++mt)
+        O[mt] = mfma(__builtin_bit_cast(bf16x8, S.af[tri_frag(mt, kb) * 64 + lane]), ub[kb], O[mt]);
+
+    // h <- exp(G_n) h + K^T diag(exp(G_n - G)) uc
+    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
+#pragma unroll
+    for (int m = 0; m < 8; ++m) H[m] *= en;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) D[mt] *= *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
+    bf16x8 Dh[2], Dl[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) split_tiles(D[2 * kb], D[2 * kb + 1], m0, m1, Dh[kb], Dl[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 ka[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ka[m] = __builtin_bit_cast(bf16x8, S.kt[(2 * m + kb) * 64 + lane]);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[m], Dh[kb], H[m]);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[m], Dl[kb], H[m]);
+    }
+
+    // output: bf16, turned by an identity product so a lane holds 4
+    // consecutive columns of one token, 8-byte stores of token rows
+    {
+      char *oc = reinterpret_cast<char *>(p.out + (s.tok0 + int64_t(c) * kChunk) * orow + int64_t(h) * kDim);
+      const uint32_t opitch = uint32_t(orow) * 2u, ocol = 2u * uint32_t(colw + 4 * q4);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 oa = chain_frag(O[2 * kk], O[2 * kk + 1]);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 d = mfma(oa, hf ? C1 : C0, zero4());
+          const int t = 32 * kk + 16 * hf + r16;
+          if (t < n) *reinterpret_cast<u32x2 *>(oc + uint32_t(t) * opitch + ocol) = pack4_bf16(d[0], d[1], d[2], d[3]);
+        }
+      }
+    }
+
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) hp[perm_dk(16 * m + 4 * q4 + ii) * kDim + colw + r16] = H[m][ii];
+}
+
+namespace {
+int compute_units() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+template <int kStrips>
+hipError_t launch_with(const Params &p, hipStream_t stream) {
+  const int r = p.nv / p.nk;
+  const int kgroups = p.B * p.nk;
+  const int blocks = 8 * ((kgroups + 7) / 8) * r * (8 / kStrips);
+  hipLaunchKernelGGL(chunk_delta_h_fwd_o<kStrips>, dim3(blocks), dim3((kStrips + 4) * 64), 0, stream, p);
+  return hipGetLastError();
+}
+} // namespace
+
+// Strips per workgroup: the fewest that keep the grid within one workgroup per
+// compute unit (the stage's LDS allows one per CU), so chains with few heads
+// spread over more CUs and many chains share LDS-staged tiles.
+hipError_t launch_stage2(const Params &p, hipStream_t stream) {
+  const long chains = long(p.B) * p.nv;
+  const int cus = compute_units();
+  if (chains * 8 <= cus) return launch_with<1>(p, stream);
+  if (chains * 4 <= cus) return launch_with<2>(p, stream);
+  return launch_with<4>(p, stream);
+}
+
+} // namespace gdn

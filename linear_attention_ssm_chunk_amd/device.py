@@ -141,11 +141,9 @@ class DeviceProblem:
         if name == "dec":
             return self.scratch[off:off + S * 2 * CHUNK * 4].view(torch.float32).view(S, 2, CHUNK)
         if name == "tp":
-            return self.scratch[off:off + S * 2 * 8 * 64 * 8 * 2].view(torch.bfloat16).view(S, 2, 8, 64, 8)
+            return self.scratch[off:off + S * 2 * 6 * 64 * 8 * 2].view(torch.bfloat16).view(S, 2, 6, 64, 8)
         if name == "s_entry":
             return self.scratch[off:off + S * HEAD_DIM * HEAD_DIM * 2].view(torch.bfloat16).view(S, HEAD_DIM, HEAD_DIM)
-        if name == "uc":
-            return self.scratch[off:off + S * HEAD_DIM * CHUNK * 2].view(torch.bfloat16).view(S, HEAD_DIM, CHUNK)
         raise KeyError(name)
 
     def slot(self, i, h, c):

@@ -112,11 +112,11 @@ def test_prefill_rejects_without_touching_the_gpu():
                       a["scratch_bytes"], a["B"], a["T"], a["nk"], a["nv"], 64, 128, a["strides"], None, 0)
     assert e.value.code == B.GDN_EUNSUPPORTED
     with pytest.raises(B.GdnError) as e:
-        B.gdn_prefill_stage(4, *[good_args()[k] for k in ("q", "k", "v", "g", "beta", "h_state",
+        B.gdn_prefill_stage(3, *[good_args()[k] for k in ("q", "k", "v", "g", "beta", "h_state",
                                                             "h_state_is_table", "out", "scratch",
                                                             "scratch_bytes", "B", "T", "nk", "nv", "dk",
                                                             "dv", "strides", "varlen")], 0)
-    assert "stage=4" in str(e.value)
+    assert "stage=3" in str(e.value)
 
 
 def test_scratch_layout_arithmetic():
@@ -126,10 +126,8 @@ def test_scratch_layout_arithmetic():
     assert L.slots == slots and L.gc == 0
     assert L.dec == slots * 64 * 4
     assert L.tp == L.dec + slots * 2 * 64 * 4
-    assert L.s_entry == L.tp + slots * 8 * 64 * 16 * 2
-    assert L.uc == L.s_entry + slots * 128 * 128 * 2
-    assert L.kfr == L.uc + slots * 128 * 64 * 2
-    assert L.total == L.kfr + chunks * 16 * 2 * 128 * 64 * 2
+    assert L.s_entry == L.tp + slots * 2 * 6 * 64 * 16
+    assert L.total == L.s_entry + slots * 128 * 128 * 2
     assert B.gdn_prefill_scratch_bytes(2, 0, 2, 4, 128, 128, B.gdn_varlen(P, P, 0, 0)) == 256
     # partial last chunk: T = 200 -> 4 chunks
     assert B.gdn_prefill_scratch_layout(1, 200, 1, 1, 128, 128).slots == 4

@@ -114,7 +114,7 @@ def test_stages_in_order_equal_one_call(dev):
     p = I.make_problem([190], nk=1, nv=2, seed=16)
     a = run(dev, p)
     b = dev(p)
-    for st in (1, 2, 3):
+    for st in (1, 2):
         b.run_stage(st)
     torch.cuda.synchronize()
     assert torch.equal(a.out, b.out) and torch.equal(a.h, b.h)
