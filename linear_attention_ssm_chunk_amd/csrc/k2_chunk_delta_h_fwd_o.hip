@@ -26,10 +26,12 @@
 //     it into the free half of a double-buffered LDS stage, from registers it
 //     filled two steps earlier, then fetches chunk c+3:
 //       - wave 0 of the pair: Q and K as whole rows (1 KB per load), written
-//         to LDS row tiles; from the row fragments it reads back, the causal
-//         decayed scores A and K^T (identity products) on MFMA;
-//       - wave 1 of the pair: the T' fragments, the decays, and V turned by
-//         identity products into the compute waves' C-tile order.
+//         to LDS row tiles, and from the row fragments it reads back, the
+//         causal decayed scores A on MFMA;
+//       - wave 1 of the pair: the T' fragments, the decays, and V as whole
+//         rows.
+//     The compute waves read K^T and their V tiles out of the row tiles with
+//     transposing LDS reads.
 // One barrier per chunk.  Entry states leave as 16-byte pieces (dk order
 // perm_dk); outputs as 8-byte pieces of whole token rows after an identity
 // product.
@@ -46,19 +48,35 @@
 
 namespace gdn {
 
-// Q and K tiles are kept as rows (64 rows of 16 pieces of 16 bytes), piece p of
-// row t at slot 16t + (p ^ (t % 16)): a whole row is written by 16 lanes at
-// once, and a row fragment (16 rows, one piece each) is read, without bank
-// conflicts.
-__device__ __forceinline__ int row_slot(int t, int piece) { return 16 * t + (piece ^ (t & 15)); }
+// Q and K tiles are kept as rows: 64 rows of 16 pieces of 16 bytes, piece p of
+// row t at slot 16t + (p ^ sig(t % 16)), sig swapping the two bit pairs of a
+// 4-bit row index.  Without bank conflicts, 16 lanes then write a whole row,
+// read a row fragment (16 rows, one piece each), or read with the transposing
+// load a 4 x 4 block of 8-byte half pieces (rows t0..t0+3, pieces p0..p0+3,
+// t0 and p0 multiples of 4).
+__device__ __forceinline__ int row_slot(int t, int piece) {
+  return 16 * t + (piece ^ (((t & 3) << 2) | ((t >> 2) & 3)));
+}
+// The V tile: 64 rows of (up to) 8 pieces, the workgroup's 64 columns; piece p
+// of row t at slot 8t + (p ^ (2 * ((t >> 1) & 1))).
+__device__ __forceinline__ int vrow_slot(int t, int piece) { return 8 * t + (piece ^ (2 * ((t >> 1) & 1))); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives, as element e, element i % 4 of the four 16-bit values that lane
+// 4e + i / 4 of its group addresses.
+__device__ __forceinline__ u32x2 read_tr(const void *lds_base, int byte_off) {
+  const lds_s16x4 *a = (const lds_s16x4 *)((const __attribute__((address_space(3))) char *)lds_base + byte_off);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a));
+}
 
 struct Stage {
-  u32x4 kr[64 * 16];          // K rows: A operand of K h (fragment (mt, kb): rows 16mt + r16, piece 4kb + q)
-  u32x4 qr[64 * 16];          // Q rows: A operand of Q h
-  u32x4 kt[16 * 64];          // K^T, A operand of K^T uc: fragment 2m + kb (rows in perm_dk order)
+  u32x4 kr[64 * 16];          // K rows: row fragments for K h and the scores, K^T for K^T uc
+  u32x4 qr[64 * 16];          // Q rows: row fragments for Q h and the scores
   u32x4 tp[2 * kTpFrags * 64]; // T' fragments: 6 hi, then 6 lo
   u32x4 af[kTpFrags * 64];    // scores A, A operand of A uc: fragment tri_frag(mt, kb)
-  u32x2 vt[4 * 4 * 64];       // V in C-tile order: (strip, mt), lane -> 4 rows of its column
+  u32x4 vr[64 * 8];           // V rows, the workgroup's columns
   float dec[2 * kChunk];      // exp(G_t), exp(G_{n-1} - G_t)
 };
 
@@ -112,7 +130,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     const int nrow = lane >> 4, piece = lane & 15; // whole-row loads: 4 rows per instruction
 
     if (role == 0) {
-      // ---- Q, K rows; the scores and K^T from them --------------------------
+      // ---- Q, K rows, and the scores from them --------------------------------
       u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
       float gt[4];          // G at t = 16mt + r16
       f32x4 gs[4];          // G at s = 16ms + 4q .. +3
@@ -139,7 +157,6 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
           gs[m] = *reinterpret_cast<const f32x4 *>(gc + 16 * m + 4 * q4);
         }
       };
-      const bf16x8 P0 = ident_perm(lane, 0), P1 = ident_perm(lane, 1);
       auto stash = [&](Stage &S) {
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
@@ -185,21 +202,6 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
             S.af[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[0], sc[1]));
           }
         }
-        // K^T fragment (m, kb): rows dk = perm_dk(16m + r16), tokens 32kb +
-        // chain order: the C tiles of row fragments (2kb, m/2) and (2kb+1, m/2)
-        // times the column picker of half m % 2.
-#pragma unroll
-        for (int kd = 0; kd < 4; ++kd)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 f0 = frag(S.kr, 2 * kb, kd), f1 = frag(S.kr, 2 * kb + 1, kd);
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const f32x4 c0 = mfma(f0, hf ? P1 : P0, zero4());
-              const f32x4 c1 = mfma(f1, hf ? P1 : P0, zero4());
-              S.kt[(2 * (2 * kd + hf) + kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(c0, c1));
-            }
-          }
       };
       if (pair < s.nchunks) fetch(pair);
       if (pair == 0) {
@@ -217,13 +219,14 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       return;
     }
 
-    // ---- T', decays, V -----------------------------------------------------
+    // ---- T', decays, V rows --------------------------------------------------
     u32x4 tx[2 * kTpFrags];
     float d0 = 0.f, d1 = 0.f;
-    // V fragments: vx[mt][blk] = V[16mt + r16][col0 + 32blk + 8q .. +7]
-    constexpr int kBlk = (kStrips + 1) / 2; // 32-column blocks (a 1-strip group reads 32, uses 16)
-    u32x4 vx[4][kBlk];
-    const int vcol = (kStrips == 1 ? (col0 & ~31) : col0) + 8 * q4; // lane's first column
+    // V rows of the workgroup's 16 * kStrips columns: 2 * kStrips pieces per row,
+    // 32 / kStrips rows per load; vx[jj] = piece vpiece of row vrow0 + jj * vrows
+    constexpr int kVPieces = 2 * kStrips, kVRows = 64 / kVPieces;
+    const int vpiece = lane % kVPieces, vrow0 = lane / kVPieces;
+    u32x4 vx[kVPieces];
     auto fetch = [&](int c) {
       const int64_t sl = slot_of(p, s, h, c);
       const u32x4 *tsrc = reinterpret_cast<const u32x4 *>(p.tp + sl * (kTpBytes / 2));
@@ -232,31 +235,21 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       d0 = p.dec[sl * 2 * kChunk + lane];
       d1 = p.dec[sl * 2 * kChunk + kChunk + lane];
       const int nn = min(kChunk, s.len - c * kChunk);
-      const char *vc = reinterpret_cast<const char *>(p.v + (s.tok0 + int64_t(c) * kChunk) * p.v_row + int64_t(h) * kDim);
+      const char *vc = reinterpret_cast<const char *>(p.v + (s.tok0 + int64_t(c) * kChunk) * p.v_row + int64_t(h) * kDim + col0);
       const uint32_t pitch = uint32_t(p.v_row) * 2u;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint32_t off = uint32_t(min(16 * mt + r16, nn - 1)) * pitch + 2u * vcol;
-#pragma unroll
-        for (int bk = 0; bk < kBlk; ++bk) vx[mt][bk] = *reinterpret_cast<const u32x4 *>(vc + off + 64u * bk);
+      for (int jj = 0; jj < kVPieces; ++jj) {
+        const uint32_t off = uint32_t(min(vrow0 + jj * kVRows, nn - 1)) * pitch + 16u * vpiece;
+        vx[jj] = *reinterpret_cast<const u32x4 *>(vc + off);
       }
     };
-    const bf16x8 I0 = ident_contig(lane, 0), I1 = ident_contig(lane, 1);
     auto stash = [&](Stage &S) {
 #pragma unroll
       for (int f = 0; f < 2 * kTpFrags; ++f) S.tp[f * 64 + lane] = tx[f];
       S.dec[lane] = d0;
       S.dec[kChunk + lane] = d1;
-      // V tile (strip w, mt): lane (q, r16) gets V[16mt + 4q .. +3][strip column r16]
 #pragma unroll
-      for (int w = 0; w < kStrips; ++w) {
-        const int cw = (kStrips == 1 ? (col0 & 31) : 16 * w); // strip offset in the fetched block
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 c0 = mfma(__builtin_bit_cast(bf16x8, vx[mt][cw >> 5]), ((cw >> 4) & 1) ? I1 : I0, zero4());
-          S.vt[(w * 4 + mt) * 64 + lane] = pack4_bf16(c0[0], c0[1], c0[2], c0[3]);
-        }
-      }
+      for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
     if (pair < s.nchunks) fetch(pair);
     if (pair == 0) {
@@ -338,7 +331,8 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       eg[mt] = *reinterpret_cast<const f32x4 *>(S.dec + 16 * mt + 4 * q4);
-      const u32x2 vv = S.vt[(wave * 4 + mt) * 64 + lane];
+      // V[16mt + 4q + ii][colw + r16], ii = 0..3: a transposing read of the V rows
+      const u32x2 vv = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const uint32_t pr = vv[ii >> 1];
@@ -393,7 +387,15 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     for (int kb = 0; kb < 2; ++kb) {
       bf16x8 ka[8];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) ka[m] = __builtin_bit_cast(bf16x8, S.kt[(2 * m + kb) * 64 + lane]);
+      for (int m = 0; m < 8; ++m) {
+        // K^T fragment (m, kb): row dk = perm_dk(16m + r16), tokens 32kb + chain
+        // order -- two transposing reads of the K rows
+        const int pc = 4 * (m >> 1) + (r16 & 3), hb = 8 * (m & 1);
+        const int t0 = 32 * kb + 4 * q4 + (r16 >> 2);
+        const u32x2 lo = read_tr(S.kr, row_slot(t0, pc) * 16 + hb);
+        const u32x2 hi = read_tr(S.kr, row_slot(t0 + 16, pc) * 16 + hb);
+        ka[m] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
 #pragma unroll
       for (int m = 0; m < 8; ++m) H[m] = mfma(ka[m], Dh[kb], H[m]);
 #pragma unroll
