@@ -33,8 +33,9 @@
 //     The compute waves read K^T and their V tiles out of the row tiles with
 //     transposing LDS reads.
 // One barrier per chunk.  Entry states leave as 16-byte pieces (dk order
-// perm_dk); outputs as 8-byte pieces of whole token rows after an identity
-// product.
+// perm_dk).  Outputs are turned by an identity product into 8-byte pieces of
+// token rows, gathered per chunk in an LDS tile, and stored by the idle
+// loader pair as whole row segments of the workgroup's columns.
 // Precision: h is float32 between chunks; h, R and the decayed uc are split
 // into bf16 hi+lo for the products that feed the state (K is exact in bf16, T'
 // arrives split), so every product keeps ~2^-17 relative error with bf16 MFMA
@@ -122,6 +123,14 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   const int col0 = cg * 16 * kStrips; // first column of this workgroup
 
   __shared__ Stage st[2];
+  // Output tiles of the last two chunks, [token][workgroup column] bf16 with a
+  // row pitch of 32 * kStrips + 16 bytes (16 rows of one column block fall in
+  // distinct banks).  A compute wave writes its strip of chunk c into tile
+  // c % 2; during step c+1 the idle loader pair stores whole row segments of
+  // it; tile c % 2 is next written in step c+2, after the barrier that ends
+  // step c+1.
+  constexpr int kOPitch = 32 * kStrips + 16;
+  __shared__ __align__(16) char ost[2][kChunk * kOPitch];
 
   // =========================== loader waves ===============================
   if (wave >= kStrips) {
@@ -169,37 +178,46 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
           return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
         };
         // C(ms, mt)[s][t] = q_t . k_s: A = K rows s, B = Q rows t; lane holds
-        // column t = 16mt + r16, rows s = 16ms + 4q .. +3.  Masked to s <= t and
-        // decayed by exp(G_t - G_s), two vertically stacked tiles are the
-        // chain-order A fragment (mt, kb) of A uc.
+        // column t = 16mt + r16, rows s = 16ms + 4q .. +3.  All Q fragments are
+        // held; each K row tile is read once and used for every mt >= ms.
+        bf16x8 qf[16];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) qf[4 * mt + kk] = frag(S.qr, mt, kk);
+        f32x4 sc[4][4]; // sc[mt][ms], ms <= mt
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+          bf16x8 kf[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) kf[kk] = frag(S.kr, ms, kk);
+#pragma unroll
+          for (int mt = ms; mt < 4; ++mt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[kk], qf[4 * mt + kk], acc);
+            sc[mt][ms] = acc;
+          }
+        }
+        // masked to s <= t and decayed by exp(G_t - G_s), two vertically
+        // stacked tiles are the chain-order A fragment (mt, kb) of A uc
         constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int t = 16 * mt + r16;
           const float g2t = gt[mt] * kLog2e;
-          bf16x8 qf[4];
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) qf[kk] = frag(S.qr, mt, kk);
+          for (int ms = 0; ms <= mt; ++ms)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const int si = 16 * ms + 4 * q4 + ii;
+              sc[mt][ms][ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - gs[ms][ii] * kLog2e) * sc[mt][ms][ii] : 0.f;
+            }
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             if (2 * kb > mt) continue;
-            f32x4 sc[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const int ms = 2 * kb + hf;
-              f32x4 acc = zero4();
-              if (ms <= mt) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma(frag(S.kr, ms, kk), qf[kk], acc);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                  const int si = 16 * ms + 4 * q4 + ii;
-                  acc[ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - gs[ms][ii] * kLog2e) * acc[ii] : 0.f;
-                }
-              }
-              sc[hf] = acc;
-            }
-            S.af[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[0], sc[1]));
+            const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
+            S.af[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
           }
         }
       };
@@ -251,6 +269,20 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
       for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
+    // outputs of chunk co (staged in tile co % 2): whole row segments of the
+    // workgroup's columns, 2 * kStrips pieces of 16 bytes per token row
+    const int64_t orow = int64_t(p.nv) * kDim;
+    auto store_out = [&](int co) {
+      const int nn = min(kChunk, s.len - co * kChunk);
+      char *oc = reinterpret_cast<char *>(p.out + (s.tok0 + int64_t(co) * kChunk) * orow + int64_t(h) * kDim + col0);
+      const uint32_t opitch = uint32_t(orow) * 2u;
+#pragma unroll
+      for (int jj = 0; jj < kVPieces; ++jj) {
+        const int t = vrow0 + jj * kVRows;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(&ost[co & 1][t * kOPitch + 16 * vpiece]);
+        if (t < nn) *reinterpret_cast<u32x4 *>(oc + uint32_t(t) * opitch + 16u * vpiece) = val;
+      }
+    };
     if (pair < s.nchunks) fetch(pair);
     if (pair == 0) {
       stash(st[0]);
@@ -262,8 +294,11 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         stash(st[(c + 1) & 1]);
         if (c + 3 < s.nchunks) fetch(c + 3);
       }
+      // the idle pair stores the previous chunk's outputs
+      if ((c & 1) == pair && c >= 1) store_out(c - 1);
       __syncthreads();
     }
+    if ((s.nchunks & 1) == pair) store_out(s.nchunks - 1);
     return;
   }
 
@@ -281,14 +316,12 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   asm volatile("" : "+v"(m0));
   asm volatile("" : "+v"(m1));
   const bf16x8 C0 = ident_chain(lane, 0), C1 = ident_chain(lane, 1);
-  const int64_t orow = int64_t(p.nv) * kDim;
 
   __syncthreads(); // chunk 0 staged
 
   for (int c = 0; c < s.nchunks; ++c) {
     const Stage &S = st[c & 1];
     const int64_t sl = slot_of(p, s, h, c);
-    const int n = min(kChunk, s.len - c * kChunk);
 
     // h -> hi/lo bf16, chain order over dk (a lane's eight values are dk
     // 32kb + 8q .. +7); bf16(h) is also the entry state
@@ -403,10 +436,9 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     }
 
     // output: bf16, turned by an identity product so a lane holds 4
-    // consecutive columns of one token, 8-byte stores of token rows
+    // consecutive columns of one token, into this chunk's output tile
     {
-      char *oc = reinterpret_cast<char *>(p.out + (s.tok0 + int64_t(c) * kChunk) * orow + int64_t(h) * kDim);
-      const uint32_t opitch = uint32_t(orow) * 2u, ocol = 2u * uint32_t(colw + 4 * q4);
+      char *ot = &ost[c & 1][32 * wave + 8 * q4];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const bf16x8 oa = chain_frag(O[2 * kk], O[2 * kk + 1]);
@@ -414,7 +446,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         for (int hf = 0; hf < 2; ++hf) {
           const f32x4 d = mfma(oa, hf ? C1 : C0, zero4());
           const int t = 32 * kk + 16 * hf + r16;
-          if (t < n) *reinterpret_cast<u32x2 *>(oc + uint32_t(t) * opitch + ocol) = pack4_bf16(d[0], d[1], d[2], d[3]);
+          *reinterpret_cast<u32x2 *>(ot + t * kOPitch) = pack4_bf16(d[0], d[1], d[2], d[3]);
         }
       }
     }
