@@ -1,12 +1,19 @@
 """Throughput of the chunked gated-delta-rule prefill on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--workload 3]
 
 One step = one gdn_prefill call (both kernels: stage 1, then the spine with the
 output fused in) over the whole synthetic workload, inputs resident in HBM.  Default workload: B=4 sequences of T=8192
 tokens, nk=16 k-heads, nv=32 v-heads, dk=dv=128, carried float32 state updated
 in place, per-chunk entry states emitted (the T=8192 workload the target is
 stated on).  Prints one JSON line.
+
+Warm-up: the W untimed warm-up steps run first; if they took less than 50 ms
+of GPU time, untimed steps continue until 50 ms have passed.  An idle MI355X
+sits in a low-power state, and the first ~25 ms of this workload run 5-40 %
+slower than the steady state while clocks settle; the timed K steps are then
+all at steady state.  The line reports the warm-up actually run
+("warmup_steps_run", "warmup_ms").
 
 roofline: the dominant kernel's algorithmic bytes per launch (the byte model
 below, per token-head / per slot, times the units one launch processes) over
@@ -31,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN chunked prefill tokens/sec on 1 MI355X; % bf16 MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+WARMUP_MIN_S = 0.05            # untimed warm-up floor: clocks reach steady state (see docstring)
 KERNELS = {1: "chunk_cumsum_recompute_wu", 2: "chunk_delta_h_fwd_o"}
 KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h_fwd_o.hip"}
 
@@ -164,8 +172,8 @@ def cpu_baseline(p, seconds_per_worker=1.5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -202,9 +210,17 @@ def main():
         kw = dict(state="table", ragged=True)
     dp = DeviceProblem(p, **kw)
 
-    for _ in range(args.warmup):
-        dp.run()
-    torch.cuda.synchronize()
+    # warm-up: W steps, then more untimed steps until 50 ms of GPU time have run
+    warm_t0 = time.perf_counter()
+    warm_steps = 0
+    while True:
+        for _ in range(max(args.warmup - warm_steps, 1) if warm_steps < args.warmup else 10):
+            dp.run()
+            warm_steps += 1
+        torch.cuda.synchronize()
+        if warm_steps >= args.warmup and time.perf_counter() - warm_t0 >= WARMUP_MIN_S:
+            break
+    warm_ms = (time.perf_counter() - warm_t0) * 1e3
 
     stages = sorted(KERNELS)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
@@ -241,6 +257,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_ms": round(warm_ms, 1),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
