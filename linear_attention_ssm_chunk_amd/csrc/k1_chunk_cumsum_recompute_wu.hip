@@ -15,7 +15,8 @@
 // One wave per (chunk, v-head):
 //   * lane t scans g; emits gc, exp(G_t) and exp(G_{n-1} - G_t);
 //   * the lower 10 tiles of K K^T on bf16 MFMA (K is exact in bf16) -> L (f32,
-//     LDS);
+//     LDS, its three lower 32x32 blocks only: 14 KB, so that 11 workgroups
+//     fit a CU);
 //   * the two diagonal 32x32 blocks of T = (I+L)^-1 by f32 forward
 //     substitution, one lane per column (32 rows, <= 496 FMAs per lane);
 //   * the off-diagonal block T21 = -T22 (L21 T11) on MFMA, every operand split
@@ -27,8 +28,7 @@
 
 namespace gdn {
 
-constexpr int kLP = 68; // L / T tile pitch (floats)
-constexpr int kTP = 36; // T11 transposed pitch (floats)
+constexpr int kBP = 36; // pitch (floats) of the 32x32 L / T blocks
 
 __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
@@ -41,9 +41,16 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
   const int lane = threadIdx.x;
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  __shared__ __align__(16) float Ls[kChunk * kLP];
-  __shared__ __align__(16) float Tt[32 * kTP];
+  // The three 32x32 blocks of the lower-triangular L, overwritten in place by
+  // the blocks of T = (I + L)^-1: B[0] = L11 / T11 (rows 0..31, columns 0..31),
+  // B[1] = L21 / T21 (rows 32..63, columns 0..31), B[2] = L22 / T22 (rows
+  // 32..63, columns 32..63).  T12 = 0 is never stored.
+  __shared__ __align__(16) float Bk[3][32 * kBP];
   __shared__ float Gs[kChunk], Bs[kChunk];
+  // element (r, s), r >= s / 32 * 32, of L / T
+  auto at = [&](int r, int sc) -> float * {
+    return &Bk[r < 32 ? 0 : (sc < 32 ? 1 : 2)][(r & 31) * kBP + (sc & 31)];
+  };
 
   // ---- K rows in the contiguous k order: kf[m][kb] = K[16m + r16][32kb + 8q .. +7]
   const uint16_t *kbase = p.k + row0 * p.qk_row + int64_t(kh) * kDim;
@@ -90,19 +97,20 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * mr + 4 * q4 + ii;
-        Ls[r * kLP + sc] = (sc < r) ? Bs[r] * expf(Gs[r] - Gs[sc]) * acc[ii] : 0.f;
+        *at(r, sc) = (sc < r) ? Bs[r] * expf(Gs[r] - Gs[sc]) * acc[ii] : 0.f;
       }
     }
 
   // ---- diagonal blocks: T_bb = (I + L_bb)^-1, lane j owns column j of block
   // b = j / 32:  T[r][j] = delta_rj - sum_{s<r} L[r][s] T[s][j] -------------
   {
-    const int b = lane >> 5, jj = lane & 31, base = 32 * b;
+    const int b = lane >> 5, jj = lane & 31;
+    float *blk = Bk[b ? 2 : 0];
     float t[32];
 #pragma unroll
     for (int rr = 0; rr < 32; ++rr) {
       float a0 = (rr == jj) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      const float *Lr = Ls + (base + rr) * kLP + base;
+      const float *Lr = blk + rr * kBP;
 #pragma unroll
       for (int s4 = 0; s4 < rr / 4; ++s4) {
         const f32x4 lv = *reinterpret_cast<const f32x4 *>(Lr + 4 * s4);
@@ -115,28 +123,19 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
       for (int s1 = 4 * (rr / 4); s1 < rr; ++s1) a0 -= Lr[s1] * t[s1];
       t[rr] = (a0 + a1) + (a2 + a3);
     }
-    // T11 and T22 row-major in place of L11 and L22 (their reads are done);
-    // T12 = 0; T11 also transposed for the B operand below.
+    // T11 and T22 in place of L11 and L22 (their reads are done)
 #pragma unroll
-    for (int rr = 0; rr < 32; ++rr) Ls[(base + rr) * kLP + base + jj] = t[rr];
-    if (b == 1) {
-#pragma unroll
-      for (int rr = 0; rr < 32; ++rr) Ls[rr * kLP + 32 + jj] = 0.f;
-    } else {
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-        *reinterpret_cast<f32x4 *>(Tt + jj * kTP + 4 * a) =
-            f32x4{t[4 * a], t[4 * a + 1], t[4 * a + 2], t[4 * a + 3]};
-    }
+    for (int rr = 0; rr < 32; ++rr) blk[rr * kBP + jj] = t[rr];
   }
 
   // ---- T21 = -T22 (L21 T11): rows 32..63, columns 0..31 -------------------
   {
-    // Pm = L21 T11, contiguous k order over s in [0, 32)
+    // Pm = L21 T11, contiguous k order over s in [0, 32); T11's columns are
+    // read straight from its rows (16 lanes read 16 consecutive floats)
     f32x4 Pm[2][2];
 #pragma unroll
     for (int mp = 0; mp < 2; ++mp) {
-      const float *ar = Ls + (32 + 16 * mp + r16) * kLP + 8 * q4;
+      const float *ar = Bk[1] + (16 * mp + r16) * kBP + 8 * q4;
       const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
       const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 4);
       const float xa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
@@ -144,10 +143,9 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
       split8(xa, ah, al);
 #pragma unroll
       for (int np = 0; np < 2; ++np) {
-        const float *br = Tt + (16 * np + r16) * kTP + 8 * q4;
-        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(br);
-        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(br + 4);
-        const float xb[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        float xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = Bk[0][(8 * q4 + e) * kBP + 16 * np + r16];
         bf16x8 bh, bl;
         split8(xb, bh, bl);
         f32x4 acc = mfma(ah, bh, zero4());
@@ -161,7 +159,7 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
     for (int np = 0; np < 2; ++np) chain_split(Pm[0][np], Pm[1][np], ph[np], pl[np]);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const float *ar = Ls + (32 + 16 * mt + r16) * kLP + 32 + 4 * q4;
+      const float *ar = Bk[2] + (16 * mt + r16) * kBP + 4 * q4;
       const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
       const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 16);
       const float xa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
@@ -173,8 +171,7 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
         acc = mfma(ah, pl[np], acc);
         acc = mfma(al, ph[np], acc);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          Ls[(32 + 16 * mt + 4 * q4 + ii) * kLP + 16 * np + r16] = -acc[ii];
+        for (int ii = 0; ii < 4; ++ii) Bk[1][(16 * mt + 4 * q4 + ii) * kBP + 16 * np + r16] = -acc[ii];
       }
     }
   }
@@ -191,8 +188,8 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
       if (2 * kb > mt) continue;
       const int t = 16 * mt + r16;
       const int s0 = 32 * kb + 4 * q4, s1 = s0 + 16;
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(Ls + t * kLP + s0);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(Ls + t * kLP + s1);
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(at(t, s0));
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(at(t, s1));
       const float x[8] = {a[0] * Bs[s0], a[1] * Bs[s0 + 1], a[2] * Bs[s0 + 2], a[3] * Bs[s0 + 3],
                           b[0] * Bs[s1], b[1] * Bs[s1 + 1], b[2] * Bs[s1 + 2], b[3] * Bs[s1 + 3]};
       bf16x8 hi, lo;
