@@ -134,8 +134,11 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 
   // =========================== loader waves ===============================
   if (wave >= kStrips) {
-    const int pair = (wave - kStrips) >> 1; // owns chunks c with c % 2 == pair
-    const int role = (wave - kStrips) & 1;
+    // Loader li = wave - S is wave 0 of its pair (role 0) for li < 2.  With
+    // waves dealt to the four SIMDs in turn, the two role-0 waves (the heavy
+    // ones) then share no SIMD with a compute wave when S <= 2.
+    const int pair = (wave - kStrips) & 1; // owns chunks c with c % 2 == pair
+    const int role = (wave - kStrips) >> 1;
     const int nrow = lane >> 4, piece = lane & 15; // whole-row loads: 4 rows per instruction
 
     if (role == 0) {
