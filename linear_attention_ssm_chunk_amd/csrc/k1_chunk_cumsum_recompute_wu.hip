@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
       if (lane >= d) G += o;
     }
     const float Gn = __shfl(G, n - 1, 64);
-    Gs[lane] = G;
+    Gs[lane] = G * 1.4426950408889634f; // log2(e) G, for exp2 below
     Bs[lane] = bv;
     p.gc[slot * kChunk + lane] = G;
     p.dec[slot * 2 * kChunk + lane] = expf(G);
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * mr + 4 * q4 + ii;
-        *at(r, sc) = (sc < r) ? Bs[r] * expf(Gs[r] - Gs[sc]) * acc[ii] : 0.f;
+        *at(r, sc) = (sc < r) ? Bs[r] * __builtin_amdgcn_exp2f(Gs[r] - Gs[sc]) * acc[ii] : 0.f;
       }
     }
 
