@@ -188,7 +188,19 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        # the same copy timed at steady clocks: the achievable read+write rate
+        for _ in range(20):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 43,
+                          "copy_ms": round(ms, 4), "copy_GBps_read_plus_write": round(2 * n * 4 / ms / 1e6, 1)}),
+              flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "

@@ -31,9 +31,15 @@ namespace gdn {
 constexpr int kBP = 36; // pitch (floats) of the 32x32 L / T blocks
 
 __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
-  const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  // Workgroup order: the r = nv/nk v-heads that read one (chunk, k-head) of K
+  // get ids 8 apart, so that on a round-robin XCD dispatch they run together
+  // on one XCD and share its L2.
+  const int r = p.nv / p.nk;
+  const int xcd = blockIdx.x & 7, round = blockIdx.x >> 3;
+  const int gidx = (round / r) * 8 + xcd; // (chunk, k-head) = (gidx / nk, gidx % nk)
+  const int c = gidx / p.nk, h = (gidx % p.nk) * r + round % r, i = blockIdx.y;
   const Seq s = seq_of(p, i);
-  if (!s.ok || c >= s.nchunks) return;
+  if (c >= p.max_chunks || !s.ok || c >= s.nchunks) return;
   const int n = min(kChunk, s.len - c * kChunk);
   const int64_t slot = slot_of(p, s, h, c);
   const int kh = (h * p.nk) / p.nv;
@@ -200,7 +206,8 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
 }
 
 hipError_t launch_stage1(const Params &p, hipStream_t stream) {
-  dim3 grid(p.max_chunks, p.nv, p.B);
+  const int64_t groups = int64_t(p.max_chunks) * p.nk; // (chunk, k-head) pairs
+  dim3 grid(unsigned(((groups + 7) / 8) * 8 * (p.nv / p.nk)), p.B);
   hipLaunchKernelGGL(chunk_cumsum_recompute_wu, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
