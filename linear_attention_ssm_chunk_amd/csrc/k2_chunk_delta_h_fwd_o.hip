@@ -106,6 +106,7 @@ __device__ __forceinline__ void split_tiles(const f32x4 &t0, const f32x4 &t1, ui
 template <int kStrips>
 __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params p) {
   constexpr int kGroups = 8 / kStrips; // workgroups per chain
+  constexpr bool kAhead = kStrips < 4;  // compute waves read LDS operands a block ahead
   // ---- which (sequence, v-head, column group) ----------------------------
   const int r = p.nv / p.nk;
   const int b = blockIdx.x;
@@ -338,67 +339,128 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<u32x4 *>(sdst + 32 * kb) = __builtin_bit_cast(u32x4, Hh[kb]);
     }
 
-    // K h  (C tile mt: column colw + r16, rows t = 16mt + 4q .. +3)
+    // K h  (C tile mt: column colw + r16, rows t = 16mt + 4q .. +3); the row
+    // fragments of block kb+1 are in flight while block kb's products issue
+    auto kfrag = [&](const u32x4 *T, int mt, int kb) {
+      return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
+    };
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    {
+      bf16x8 ka[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 ka[4];
+      for (int mt = 0; mt < 4; ++mt) ka[0][mt] = kfrag(S.kr, mt, 0);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) ka[mt] = __builtin_bit_cast(bf16x8, S.kr[row_slot(16 * mt + r16, 4 * kb + q4)]);
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb < 3) {
+          // with few compute waves per CU, read block kb+1 before block kb's
+          // products (latency hidden); with four, read it after them (fewer
+          // reads in flight at once on the shared LDS)
+          if constexpr (kAhead) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[mt], Hh[kb], acc[mt]);
+            for (int mt = 0; mt < 4; ++mt) ka[(kb + 1) & 1][mt] = kfrag(S.kr, mt, kb + 1);
+          }
+        }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[mt], Hl[kb], acc[mt]);
-    }
-    // Q h (bf16 h): the state term of the output
-    f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[kb & 1][mt], Hh[kb], acc[mt]);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 qa[4];
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[kb & 1][mt], Hl[kb], acc[mt]);
+        if constexpr (!kAhead) {
+          if (kb < 3) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) qa[mt] = __builtin_bit_cast(bf16x8, S.qr[row_slot(16 * mt + r16, 4 * kb + q4)]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(qa[mt], Hh[kb], O[mt]);
+            for (int mt = 0; mt < 4; ++mt) ka[(kb + 1) & 1][mt] = kfrag(S.kr, mt, kb + 1);
+          }
+        }
+      }
     }
 
-    // R = V - diag(exp(G)) K h
+    // R = V - diag(exp(G)) K h, split; the output's state term Q h (bf16 h)
+    // is off the dependent chain and issues among R's vector instructions
     f32x4 eg[4];
-    f32x4 R[4];
+    u32x2 vv[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       eg[mt] = *reinterpret_cast<const f32x4 *>(S.dec + 16 * mt + 4 * q4);
       // V[16mt + 4q + ii][colw + r16], ii = 0..3: a transposing read of the V rows
-      const u32x2 vv = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
+      vv[mt] = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
+    }
+    bf16x8 qa[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) qa[4 * kb + mt] = kfrag(S.qr, mt, kb);
+    f32x4 R[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const uint32_t pr = vv[ii >> 1];
+        const uint32_t pr = vv[mt][ii >> 1];
         const float v = __builtin_bit_cast(float, (ii & 1) ? (pr & 0xFFFF0000u) : (pr << 16));
         R[mt][ii] = v - eg[mt][ii] * acc[mt][ii];
       }
-    }
+    f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(qa[4 * kb + mt], Hh[kb], O[mt]);
     bf16x8 Rh[2], Rl[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) split_tiles(R[2 * kb], R[2 * kb + 1], m0, m1, Rh[kb], Rl[kb]);
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // then four VALU
+      }
+    }
 
-    // uc = T' R  (T' is lower triangular: fragment (mt, 1) is zero for mt < 2)
+    // uc = T' R  (T' is lower triangular: fragment (mt, 1) is zero for mt < 2);
+    // all T' fragments are read up front
+    bf16x8 th[kTpFrags], tl[kTpFrags];
+    auto tpfrag = [&](int f) {
+      th[f] = __builtin_bit_cast(bf16x8, S.tp[f * 64 + lane]);
+      tl[f] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + f) * 64 + lane]);
+    };
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int f = 0; f < kTpFrags; ++f) tpfrag(f);
+    }
     f32x4 D[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 th[4], tl[4];
+      if constexpr (!kAhead) {
 #pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) {
-        th[mt] = __builtin_bit_cast(bf16x8, S.tp[tri_frag(mt, kb) * 64 + lane]);
-        tl[mt] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + tri_frag(mt, kb)) * 64 + lane]);
+        for (int mt = 2 * kb; mt < 4; ++mt) tpfrag(tri_frag(mt, kb));
       }
 #pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[mt], Rh[kb], D[mt]);
+      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[tri_frag(mt, kb)], Rh[kb], D[mt]);
 #pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[mt], Rl[kb], D[mt]);
+      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[tri_frag(mt, kb)], Rl[kb], D[mt]);
 #pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(tl[mt], Rh[kb], D[mt]);
+      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(tl[tri_frag(mt, kb)], Rh[kb], D[mt]);
+    }
+    bf16x8 af[kTpFrags];
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int f = 0; f < kTpFrags; ++f) af[f] = __builtin_bit_cast(bf16x8, S.af[f * 64 + lane]);
+    }
+    // K^T fragment (m, kb): row dk = perm_dk(16m + r16), tokens 32kb + chain
+    // order -- two transposing reads of the K rows
+    auto ktfrag = [&](int m, int kb) {
+      const int pc = 4 * (m >> 1) + (r16 & 3), hb = 8 * (m & 1);
+      const int t0 = 32 * kb + 4 * q4 + (r16 >> 2);
+      const u32x2 lo = read_tr(S.kr, row_slot(t0, pc) * 16 + hb);
+      const u32x2 hi = read_tr(S.kr, row_slot(t0 + 16, pc) * 16 + hb);
+      return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    bf16x8 ka[2][8];
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ka[0][m] = ktfrag(m, 0);
     }
 
-    // O = diag(exp(G)) Q h + A bf16(uc)
+    // h <- exp(G_n) h + K^T diag(exp(G_n - G)) uc; the output's intra-chunk
+    // term A bf16(uc) issues among the vector instructions of the split
+    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
     bf16x8 ub[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) ub[kb] = chain_frag(D[2 * kb], D[2 * kb + 1]);
@@ -407,11 +469,10 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt)
-        O[mt] = mfma(__builtin_bit_cast(bf16x8, S.af[tri_frag(mt, kb) * 64 + lane]), ub[kb], O[mt]);
-
-    // h <- exp(G_n) h + K^T diag(exp(G_n - G)) uc
-    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
+      for (int mt = 2 * kb; mt < 4; ++mt) {
+        if constexpr (!kAhead) af[tri_frag(mt, kb)] = __builtin_bit_cast(bf16x8, S.af[tri_frag(mt, kb) * 64 + lane]);
+        O[mt] = mfma(af[tri_frag(mt, kb)], ub[kb], O[mt]);
+      }
 #pragma unroll
     for (int m = 0; m < 8; ++m) H[m] *= en;
 #pragma unroll
@@ -419,23 +480,35 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     bf16x8 Dh[2], Dl[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) split_tiles(D[2 * kb], D[2 * kb + 1], m0, m1, Dh[kb], Dl[kb]);
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1); // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1); // then six VALU
+      }
+    }
+    if constexpr (!kAhead) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ka[0][m] = ktfrag(m, 0);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 ka[8];
+      if constexpr (kAhead) {
+        if (kb == 0) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        // K^T fragment (m, kb): row dk = perm_dk(16m + r16), tokens 32kb + chain
-        // order -- two transposing reads of the K rows
-        const int pc = 4 * (m >> 1) + (r16 & 3), hb = 8 * (m & 1);
-        const int t0 = 32 * kb + 4 * q4 + (r16 >> 2);
-        const u32x2 lo = read_tr(S.kr, row_slot(t0, pc) * 16 + hb);
-        const u32x2 hi = read_tr(S.kr, row_slot(t0 + 16, pc) * 16 + hb);
-        ka[m] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          for (int m = 0; m < 8; ++m) ka[1][m] = ktfrag(m, 1);
+        }
       }
 #pragma unroll
-      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[m], Dh[kb], H[m]);
+      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[kb][m], Dh[kb], H[m]);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[m], Dl[kb], H[m]);
+      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[kb][m], Dl[kb], H[m]);
+      if constexpr (!kAhead) {
+        if (kb == 0) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) ka[1][m] = ktfrag(m, 1);
+        }
+      }
     }
 
     // output: bf16, turned by an identity product so a lane holds 4
