@@ -167,6 +167,116 @@ def cpu_baseline(p, seconds_per_worker=1.5):
 
 
 # ---------------------------------------------------------------------------
+# decode: one recurrent step per sequence (gdn_decode), a serving batch
+
+DECODE_METRIC = "GDN recurrent decode tokens/sec on 1 MI355X; % HBM roofline"
+DECODE_SHAPE = dict(B=256, nk=16, nv=32)
+
+
+def decode_bytes(B, nk, nv):
+    """Algorithmic bytes of one decode step: the float32 state read and
+    written (64 KB each way per head), q and k once per k-head, v, g, beta, o."""
+    d = 128
+    return B * (nv * d * d * 4 * 2 + 2 * nk * d * 2 + nv * d * 2 + nv * 8 + nv * d * 2)
+
+
+def _oracle_decode_worker(args):
+    w, workers, seconds = args
+    from threadpoolctl import threadpool_limits
+    from oracle import gdn_recurrence, kv_head_map
+    from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64
+    p = _SAMPLE_PROBLEM
+    kmap = kv_head_map(p.nk, p.nv)
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        chain = w
+        while time.perf_counter() - t0 < seconds:
+            i, h = chain % p.nseq, (chain // p.nseq) % p.nv
+            kap = kmap[[h]]
+            gdn_recurrence(bf16_to_f64(p.q[i:i + 1][:, kap]), bf16_to_f64(p.k[i:i + 1][:, kap]),
+                           bf16_to_f64(p.v[i:i + 1][:, [h]]), p.g[i:i + 1][:, [h]].astype("float64"),
+                           p.beta[i:i + 1][:, [h]].astype("float64"), p.h0[i][[h]].astype("float64"))
+            done += 1
+            chain += workers
+    return done, time.perf_counter() - t0
+
+
+def bench_decode(args):
+    import multiprocessing as mp
+    global _SAMPLE_PROBLEM
+    from linear_attention_ssm_chunk_amd import inputs as I
+    sh = DECODE_SHAPE
+    p = I.make_problem([1] * sh["B"], sh["nk"], sh["nv"], seed=6)
+    cpu = None
+    if not args.no_cpu_baseline:
+        _SAMPLE_PROBLEM = p
+        workers = max(1, min(16, os.cpu_count() or 1))
+        t0 = time.perf_counter()
+        with mp.get_context("fork").Pool(workers) as pool:
+            res = pool.map(_oracle_decode_worker, [(w, workers, 1.5) for w in range(workers)])
+        wall = time.perf_counter() - t0
+        heads = sum(r[0] for r in res)
+        cpu = {"value": heads / wall / p.nv, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+               "sample": (f"{workers} workers (one BLAS thread each) running single-token steps of this batch's "
+                          f"(sequence, v-head) pairs through the float64 recurrence for 1.5 s each: {heads} "
+                          f"head-steps, wall {wall:.1f}s; tokens/s = head-steps/s / nv")}
+    import torch
+    from linear_attention_ssm_chunk_amd.device import DeviceProblem
+    dp = DeviceProblem(p, ragged=False)
+    warm_t0 = time.perf_counter()
+    warm_steps = 0
+    while warm_steps < args.warmup or time.perf_counter() - warm_t0 < WARMUP_MIN_S:
+        for _ in range(10):
+            dp.decode_step(0)
+        warm_steps += 10
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        dp.decode_step(0)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_kernel = e0.elapsed_time(e1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    by = decode_bytes(sh["B"], sh["nk"], sh["nv"])
+    achieved = by / (ms_kernel / 1e3) / 1e9
+    line = {
+        "metric": DECODE_METRIC, "value": round(sh["B"] / (ms_per_step / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm_steps,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode_B256", "B": sh["B"], "nk": sh["nk"], "nv": sh["nv"], "dk": 128, "dv": 128,
+                   "tokens_per_sequence": 1},
+        "roofline": {"bound": "hbm", "kernel": "recurrent_decode", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for_decode()},
+        "kernels": {"recurrent_decode": {"ms": round(ms_kernel, 4), "alg_bytes": by}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def traffic_for_decode():
+    path = os.path.join(ROOT, "profiles", "traffic_recurrent_decode_decode_B256.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    src = os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", "k3_recurrent_decode.hip")
+    h = hashlib.sha256()
+    for f in (src, os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", "gdn_device.h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    if t.get("source_sha256") != h.hexdigest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
 
 
 def main():
@@ -176,6 +286,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure the recurrent decode step (gdn_decode) on a batch of 256 sequences instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (three times), to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -206,6 +318,10 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
               f"requested); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        bench_decode(args)
+        return
 
     from linear_attention_ssm_chunk_amd import inputs as I
     p = I.make_workload(args.workload)

@@ -194,6 +194,34 @@ int gdn_prefill_stage(int stage, const void *q, const void *k, const void *v, co
 int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *cu_chunks_host,
                           int32_t max_chunks, int32_t total_chunks);
 
+/*
+ * One recurrent step per sequence (decode): the token that follows a prefill,
+ * on the state the prefill leaves in place.  For each sequence b and v-head h
+ * (k-head kappa = (h * nk) / nv), with S the state, a = exp(g):
+ *     S <- a S (I - beta k k^T) + beta v k^T,     o = S q
+ * -- the recurrence of the header comment for one token (Gated DeltaNet;
+ * page "spark_model/layers/ops/ssm_gdn_a3.rs", gdn_prefill_fla's doc comment
+ * for the in-place state and its per-request table).  In the stored
+ * orientation h = S^T: delta = beta (v - a h^T k), h <- a h + k delta^T,
+ * o = h^T q.
+ *   q, k     bf16; token b's head kappa at q + b*qk_row + kappa*128.
+ *   v        bf16; head h at v + b*v_row + h*128.
+ *   g, beta  float at g[b*gb_row + h], beta[b*gb_row + h].
+ *   h_state  as for gdn_prefill (contiguous [B][nv][dk][dv], or a device
+ *            table of B pointers to [nv][dk][dv]), updated in place.
+ *   out      bf16 [B][nv][dv], contiguous.
+ * dk = dv = 128.  No scratch; one launch on `stream`, no synchronisation.
+ * Returns GDN_OK or an error as gdn_prefill does; gdn_decode_validate runs the
+ * same checks without touching the GPU.
+ */
+int gdn_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
+               void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
+               const gdn_strides *strides, void *stream);
+
+int gdn_decode_validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk,
+                        int dv, const gdn_strides *strides);
+
 /* Text of the last error on the calling thread ("" after success). */
 const char *gdn_last_error(void);
 

@@ -71,6 +71,11 @@ def lib():
         L.gdn_varlen_check_host.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                             ctypes.c_int32, ctypes.c_int32]
         L.gdn_varlen_check_host.restype = i32
+        dec = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_strides)]
+        L.gdn_decode.argtypes = dec + [vp]
+        L.gdn_decode.restype = i32
+        L.gdn_decode_validate.argtypes = dec
+        L.gdn_decode_validate.restype = i32
         L.gdn_last_error.argtypes = []
         L.gdn_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -163,3 +168,25 @@ def gdn_varlen_check_host(B, cu_seqlens, cu_chunks, max_chunks, total_chunks):
     a = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
     b = (ctypes.c_int32 * len(cu_chunks))(*[int(x) for x in cu_chunks])
     return lib().gdn_varlen_check_host(B, a, b, int(max_chunks), int(total_chunks))
+
+
+def _decode_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides):
+    st = _strides(strides)
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h_state), int(h_state_is_table), _ptr(out),
+            B, nk, nv, dk, dv, _ref(st)), st
+
+
+def gdn_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides, stream):
+    """Enqueue one recurrent step per sequence on ``stream``.  Raises GdnError on
+    a nonzero return."""
+    args, keep = _decode_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides)
+    rc = lib().gdn_decode(*args, ctypes.c_void_p(int(stream)))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return rc
+
+
+def gdn_decode_validate(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides):
+    """Return code of the decode's host validation (no exception)."""
+    args, keep = _decode_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides)
+    return lib().gdn_decode_validate(*args)

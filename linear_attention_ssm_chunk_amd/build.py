@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn_prefill.so")
-SOURCES = ["gdn_api.hip", "k1_chunk_cumsum_recompute_wu.hip", "k2_chunk_delta_h_fwd_o.hip"]
+SOURCES = ["gdn_api.hip", "k1_chunk_cumsum_recompute_wu.hip", "k2_chunk_delta_h_fwd_o.hip",
+           "k3_recurrent_decode.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",

@@ -17,6 +17,7 @@
 namespace gdn {
 hipError_t launch_stage1(const Params &p, hipStream_t stream);
 hipError_t launch_stage2(const Params &p, hipStream_t stream);
+hipError_t launch_decode(const Params &p, hipStream_t stream);
 } // namespace gdn
 
 namespace {
@@ -192,6 +193,43 @@ int run_stage(int stage, const gdn::Params &p, hipStream_t stream) {
   return ok();
 }
 
+int validate_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
+                    const gdn_strides *strides) {
+  if (dk != GDN_HEAD_DIM || dv != GDN_HEAD_DIM)
+    return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
+  if (nk <= 0 || nv <= 0) return fail(GDN_EINVAL, "head counts: nk=%d nv=%d must be positive", nk, nv);
+  if (nv % nk != 0) return fail(GDN_EINVAL, "GQA grouping: nv=%d is not a multiple of nk=%d", nv, nk);
+  if (nv > (1 << 24)) return fail(GDN_EINVAL, "nv=%d is too large for the grid", nv);
+  if (B <= 0 || B > 65535) return fail(GDN_EINVAL, "B=%d must be in 1..65535", B);
+  if (!q || !k || !v) return fail(GDN_EINVAL, "null pointer: q, k and v are required");
+  if (!g || !beta) return fail(GDN_EINVAL, "null pointer: g and beta are required");
+  if (!h_state) return fail(GDN_EINVAL, "null pointer: h_state is required");
+  if (!out) return fail(GDN_EINVAL, "null pointer: out is required");
+  if (!strides) return fail(GDN_EINVAL, "null pointer: strides is required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(GDN_EINVAL, "alignment: q, k and v must be 16-byte aligned (16-byte vector loads)");
+  if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_EINVAL, "alignment: g and beta must be 4-byte aligned");
+  if (h_state_is_table != 0 && h_state_is_table != 1)
+    return fail(GDN_EINVAL, "h_state_is_table=%d must be 0 or 1", h_state_is_table);
+  if (!aligned(h_state, h_state_is_table ? 8 : 16))
+    return fail(GDN_EINVAL, "alignment: h_state must be 16-byte aligned (8 for a pointer table)");
+  if (!aligned(out, 16)) return fail(GDN_EINVAL, "alignment: out must be 16-byte aligned");
+  if (strides->qk_row % 8 != 0 || strides->v_row % 8 != 0)
+    return fail(GDN_EINVAL,
+                "strides: qk_row=%lld and v_row=%lld must be multiples of 8 (rows are read 16 bytes at a time)",
+                (long long)strides->qk_row, (long long)strides->v_row);
+  if (strides->qk_row < int64_t(nk) * GDN_HEAD_DIM)
+    return fail(GDN_EINVAL, "strides: qk_row=%lld is smaller than nk*128=%d", (long long)strides->qk_row,
+                nk * GDN_HEAD_DIM);
+  if (strides->v_row < int64_t(nv) * GDN_HEAD_DIM)
+    return fail(GDN_EINVAL, "strides: v_row=%lld is smaller than nv*128=%d", (long long)strides->v_row,
+                nv * GDN_HEAD_DIM);
+  if (strides->gb_row < nv)
+    return fail(GDN_EINVAL, "strides: gb_row=%lld is smaller than nv=%d", (long long)strides->gb_row, nv);
+  return ok();
+}
+
 } // namespace
 
 extern "C" {
@@ -268,6 +306,38 @@ int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *
     return fail(GDN_EINVAL, "ragged: max_chunks=%d but the longest sequence has %d chunks", max_chunks, mx);
   if (cu_chunks_host[B] != total_chunks)
     return fail(GDN_EINVAL, "ragged: total_chunks=%d but cu_chunks[B]=%d", total_chunks, cu_chunks_host[B]);
+  return ok();
+}
+
+int gdn_decode_validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
+                        const gdn_strides *strides) {
+  return validate_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides);
+}
+
+int gdn_decode(const void *q, const void *k, const void *v, const float *g, const float *beta, void *h_state,
+               int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+               void *stream) {
+  int rc = validate_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides);
+  if (rc != GDN_OK) return rc;
+  gdn::Params p{};
+  p.q = static_cast<const uint16_t *>(q);
+  p.k = static_cast<const uint16_t *>(k);
+  p.v = static_cast<const uint16_t *>(v);
+  p.g = g;
+  p.beta = beta;
+  p.h_state = h_state;
+  p.h_is_table = h_state_is_table;
+  p.out = static_cast<uint16_t *>(out);
+  p.qk_row = strides->qk_row;
+  p.v_row = strides->v_row;
+  p.gb_row = strides->gb_row;
+  p.B = B;
+  p.T = 1;
+  p.nk = nk;
+  p.nv = nv;
+  const hipError_t e = gdn::launch_decode(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDN_EHIP, "launch of recurrent_decode failed: %s", hipGetErrorString(e));
   return ok();
 }
 

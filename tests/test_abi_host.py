@@ -146,3 +146,52 @@ def test_varlen_host_check():
     assert "decreases" in B.gdn_last_error()
     assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 2, 5) == B.GDN_EINVAL
     assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 3, 6) == B.GDN_EINVAL
+
+
+def decode_args(**over):
+    a = dict(q=P, k=P + 4096, v=P + 8192, g=P + 16384, beta=P + 16384 + 128, h_state=P + 2 ** 30,
+             h_state_is_table=0, out=P + 2 ** 31, B=3, nk=2, nv=4, dk=128, dv=128,
+             strides=B.gdn_strides(2 * 128, 4 * 128, 4))
+    a.update(over)
+    return a
+
+
+def decode_validate(**over):
+    a = decode_args(**over)
+    rc = B.gdn_decode_validate(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h_state"], a["h_state_is_table"],
+                               a["out"], a["B"], a["nk"], a["nv"], a["dk"], a["dv"], a["strides"])
+    return rc, B.gdn_last_error()
+
+
+def test_decode_validation_names_the_guard():
+    assert decode_validate()[0] == B.GDN_OK
+    rc, msg = decode_validate(dk=64)
+    assert rc == B.GDN_EUNSUPPORTED and "head size" in msg
+    rc, msg = decode_validate(nk=3, nv=4)
+    assert rc == B.GDN_EINVAL and "GQA" in msg
+    rc, msg = decode_validate(B=0)
+    assert rc == B.GDN_EINVAL and "B=0" in msg
+    rc, msg = decode_validate(q=0)
+    assert rc == B.GDN_EINVAL and "null pointer" in msg
+    rc, msg = decode_validate(out=0)
+    assert rc == B.GDN_EINVAL and "out" in msg
+    rc, msg = decode_validate(k=P + 8)
+    assert rc == B.GDN_EINVAL and "alignment" in msg
+    rc, msg = decode_validate(h_state_is_table=2)
+    assert rc == B.GDN_EINVAL and "h_state_is_table" in msg
+    rc, msg = decode_validate(strides=B.gdn_strides(2 * 128 + 4, 4 * 128, 4))
+    assert rc == B.GDN_EINVAL and "multiples of 8" in msg
+    rc, msg = decode_validate(strides=B.gdn_strides(128, 4 * 128, 4))
+    assert rc == B.GDN_EINVAL and "qk_row" in msg
+    rc, msg = decode_validate(strides=B.gdn_strides(2 * 128, 4 * 128, 3))
+    assert rc == B.GDN_EINVAL and "gb_row" in msg
+    # a table of state pointers only needs 8-byte alignment
+    assert decode_validate(h_state=P + 8, h_state_is_table=1)[0] == B.GDN_OK
+
+
+def test_decode_rejects_without_touching_the_gpu():
+    a = decode_args(nv=5)
+    with pytest.raises(B.GdnError) as e:
+        B.gdn_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h_state"], 0, a["out"], a["B"], a["nk"],
+                     a["nv"], 128, 128, a["strides"], 0)
+    assert e.value.code == B.GDN_EINVAL

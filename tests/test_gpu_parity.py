@@ -242,3 +242,99 @@ def test_slow_decay_long_carry(dev):
     w = check_problem(dp, p, intermediates=True)
     print(w)
     assert_within(w, intermediates=True)
+
+
+# --------------------------------------------------------------------------
+# decode: one recurrent step per sequence (gdn_decode)
+
+def _decode_run(DP, p, steps, **kw):
+    """Decode every token of p one step at a time; returns the outputs
+    [T][B][nv][dv] (float) and the device problem (state after the last step)."""
+    print(f"[gpu] decode lengths={p.lengths} nk={p.nk} nv={p.nv} {kw}", flush=True)
+    dp = DP(p, ragged=False, **kw)
+    outs = []
+    for t in range(steps):
+        dp.decode_step(t)
+        torch.cuda.synchronize()
+        outs.append(dp.dec_out.float().cpu().numpy())
+    return np.stack(outs), dp
+
+
+def _oracle_steps(p):
+    """Oracle outputs [T][B][nv][dv] and final states of every sequence."""
+    from parity import seq_arrays
+    from oracle import gdn_recurrence
+    T = p.lengths[0]
+    o = np.zeros((T, p.nseq, p.nv, 128))
+    hs = []
+    for i in range(p.nseq):
+        oi, hi, _ = gdn_recurrence(**seq_arrays(p, i))
+        o[:, i] = oi
+        hs.append(hi)
+    return o, np.stack(hs)
+
+
+@pytest.mark.parametrize("nk,nv", [(2, 6), (1, 1)])
+def test_decode_one_token(dev, nk, nv):
+    p = I.make_problem([1] * 5, nk=nk, nv=nv, seed=700 + nv)
+    out, dp = _decode_run(dev, p, 1)
+    o_ref, h_ref = _oracle_steps(p)
+    assert np.abs(out - o_ref).max() <= 2e-2
+    st = dp.state().astype(np.float64)
+    assert max(relfro(st[i, h], h_ref[i, h]) for i in range(p.nseq) for h in range(p.nv)) <= 1e-5
+
+
+def test_decode_steps_state_table_conv(dev):
+    """Nine decode steps in a row on the packed conv layout with a state
+    table: outputs at every step and the final state against the oracle."""
+    p = I.make_problem([9] * 3, nk=1, nv=3, seed=710)
+    out, dp = _decode_run(dev, p, 9, layout="conv", state="table")
+    o_ref, h_ref = _oracle_steps(p)
+    assert np.abs(out - o_ref).max() <= 2e-2
+    st = dp.state().astype(np.float64)
+    assert max(relfro(st[i, h], h_ref[i, h]) for i in range(p.nseq) for h in range(p.nv)) <= 1e-5
+
+
+def test_decode_layouts_bit_identical(dev):
+    p = I.make_problem([4] * 2, nk=2, nv=4, seed=720)
+    a_out, a = _decode_run(dev, p, 4)
+    b_out, b = _decode_run(dev, p, 4, layout="conv", state="table")
+    assert np.array_equal(a_out, b_out) and np.array_equal(a.state(), b.state())
+
+
+def test_decode_beta_zero_only_decays(dev):
+    """beta = 0: h <- exp(g) h exactly (one float32 product), o = exp(g) h^T q."""
+    p = I.make_problem([1] * 3, nk=1, nv=2, seed=730)
+    p.beta[:] = 0
+    out, dp = _decode_run(dev, p, 1)
+    a = np.exp(p.g.astype(np.float64))  # [B][nv]
+    want = (a[:, :, None, None] * p.h0.astype(np.float64)).astype(np.float32)
+    assert np.abs(dp.state() - want).max() <= 1e-6 * np.abs(want).max()
+    o_ref, _ = _oracle_steps(p)
+    assert np.abs(out - o_ref).max() <= 2e-2
+
+
+def test_prefill_then_decode_continues_the_sequence(dev):
+    """Prefill of 130 tokens (ragged chunk tail) leaves the state in place;
+    decoding token 131 from it matches the oracle over all 131 tokens."""
+    from parity import seq_arrays
+    from oracle import gdn_recurrence
+    T = 131
+    full = I.make_problem([T] * 2, nk=2, nv=4, seed=740)
+    rows = np.concatenate([np.arange(i * T, i * T + T - 1) for i in range(2)])
+    last = np.array([i * T + T - 1 for i in range(2)])
+    pre = I.Problem([T - 1] * 2, full.nk, full.nv, full.q[rows], full.k[rows], full.v[rows], full.g[rows],
+                    full.beta[rows], full.h0.copy(), full.seed)
+    one = I.Problem([1] * 2, full.nk, full.nv, full.q[last], full.k[last], full.v[last], full.g[last],
+                    full.beta[last], full.h0.copy(), full.seed)
+    dp = run(dev, pre)
+    dd = dev(one, ragged=False)
+    dd.h.copy_(dp.h)  # the prefill's final state, in place for the next token
+    dd.decode_step(0)
+    torch.cuda.synchronize()
+    out = dd.dec_out.float().cpu().numpy()
+    st = dd.state().astype(np.float64)
+    for i in range(2):
+        o_ref, h_ref, _ = gdn_recurrence(**seq_arrays(full, i))
+        assert np.abs(out[i] - o_ref[-1]).max() <= 2e-2
+        assert max(relfro(st[i, h], h_ref[h]) for h in range(full.nv)) <= 1e-3
