@@ -31,13 +31,13 @@ namespace gdn {
 constexpr int kBP = 36; // pitch (floats) of the 32x32 L / T blocks
 
 __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
-  // Workgroup order: the r = nv/nk v-heads that read one (chunk, k-head) of K
-  // get ids 8 apart, so that on a round-robin XCD dispatch they run together
-  // on one XCD and share its L2.
-  const int r = p.nv / p.nk;
+  // Workgroup order: all nv heads of one chunk get ids 8 apart, so that on a
+  // round-robin XCD dispatch they run close together on one XCD and share its
+  // L2 -- the chunk's K rows (each read by the r = nv/nk v-heads of a k-head,
+  // which come one after another) and its g / beta rows (one row per token
+  // holds every head's value).
   const int xcd = blockIdx.x & 7, round = blockIdx.x >> 3;
-  const int gidx = (round / r) * 8 + xcd; // (chunk, k-head) = (gidx / nk, gidx % nk)
-  const int c = gidx / p.nk, h = (gidx % p.nk) * r + round % r, i = blockIdx.y;
+  const int c = (round / p.nv) * 8 + xcd, h = round % p.nv, i = blockIdx.y;
   const Seq s = seq_of(p, i);
   if (c >= p.max_chunks || !s.ok || c >= s.nchunks) return;
   const int n = min(kChunk, s.len - c * kChunk);
@@ -206,8 +206,7 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
 }
 
 hipError_t launch_stage1(const Params &p, hipStream_t stream) {
-  const int64_t groups = int64_t(p.max_chunks) * p.nk; // (chunk, k-head) pairs
-  dim3 grid(unsigned(((groups + 7) / 8) * 8 * (p.nv / p.nk)), p.B);
+  dim3 grid(unsigned(((p.max_chunks + 7) / 8) * 8 * p.nv), p.B);
   hipLaunchKernelGGL(chunk_cumsum_recompute_wu, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
