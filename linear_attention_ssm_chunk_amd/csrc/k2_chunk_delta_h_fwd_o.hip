@@ -21,21 +21,26 @@
 //     lives in MFMA accumulators; in the chain k order those registers are the
 //     B operand of K h and Q h directly, and so are the C tiles of
 //     R = V - e^G K h (for T' R) and of uc (for K^T uc and A uc): the
-//     dependent chain never leaves registers;
-//   * waves S..S+3 (loaders), two pairs; the pair that owns chunk c+1 stages
-//     it into the free half of a double-buffered LDS stage, from registers it
-//     filled two steps earlier, then fetches chunk c+3:
-//       - wave 0 of the pair: Q and K as whole rows (1 KB per load), written
-//         to LDS row tiles, and from the row fragments it reads back, the
-//         causal decayed scores A on MFMA;
-//       - wave 1 of the pair: the T' fragments, the decays, and V as whole
-//         rows.
+//     dependent chain never leaves registers.  Step c runs chunk c's chain and
+//     state term diag(exp(G)) Q h, and finishes chunk c-1's output with A uc,
+//     whose scores were formed during step c-1;
+//   * waves S..S+3 (loaders), two pairs that take turns.  In step c the
+//     active pair stages chunk c+1 into the free half of a double-buffered
+//     LDS stage, from registers it filled two steps earlier, then fetches
+//     chunk c+3: wave 0 the Q and K rows (1 KB per load), wave 1 the T'
+//     fragments, decays, gate sums and V rows.  The idle pair works on chunk
+//     c, visible in the stage compute reads: wave 1 reads back the Q and K
+//     row fragments and forms the causal decayed scores A of chunk c on MFMA;
+//     wave 0 stores the output tile of chunk c-2.
 //     The compute waves read K^T and their V tiles out of the row tiles with
 //     transposing LDS reads.
-// One barrier per chunk.  Entry states leave as 16-byte pieces (dk order
-// perm_dk).  Outputs are turned by an identity product into 8-byte pieces of
-// token rows, gathered per chunk in an LDS tile, and stored by the idle
-// loader pair as whole row segments of the workgroup's columns.
+// One barrier per chunk (and one after the last).  Entry states leave as
+// 16-byte pieces (dk order perm_dk).  Outputs are turned by an identity
+// product into 8-byte pieces of token rows, gathered per chunk in an LDS tile,
+// and stored by a loader as whole row segments of the workgroup's columns.
+// Every double-buffered region (stage, scores, output tile) is written in one
+// step and read in the next, and written again only after the barrier that
+// ends the reading step.
 // Precision: h is float32 between chunks; h, R and the decayed uc are split
 // into bf16 hi+lo for the products that feed the state (K is exact in bf16, T'
 // arrives split), so every product keeps ~2^-17 relative error with bf16 MFMA
@@ -76,9 +81,9 @@ struct Stage {
   u32x4 kr[64 * 16];          // K rows: row fragments for K h and the scores, K^T for K^T uc
   u32x4 qr[64 * 16];          // Q rows: row fragments for Q h and the scores
   u32x4 tp[2 * kTpFrags * 64]; // T' fragments: 6 hi, then 6 lo
-  u32x4 af[kTpFrags * 64];    // scores A, A operand of A uc: fragment tri_frag(mt, kb)
   u32x4 vr[64 * 8];           // V rows, the workgroup's columns
   float dec[2 * kChunk];      // exp(G_t), exp(G_{n-1} - G_t)
+  float g2[kChunk];           // log2(e) G_t, for the scores' decays
 };
 
 // Split two C tiles (a k block of 32 rows, chain order) into hi / lo bf16
@@ -106,7 +111,6 @@ __device__ __forceinline__ void split_tiles(const f32x4 &t0, const f32x4 &t1, ui
 template <int kStrips>
 __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params p) {
   constexpr int kGroups = 8 / kStrips; // workgroups per chain
-  constexpr bool kAhead = kStrips < 4;  // compute waves read LDS operands a block ahead
   // ---- which (sequence, v-head, column group) ----------------------------
   const int r = p.nv / p.nk;
   const int b = blockIdx.x;
@@ -118,35 +122,38 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   const int h = kh * r + j;
   const Seq s = seq_of(p, i);
   if (!s.ok || s.nchunks == 0) return; // length 0: the state is left as it is
+  const int nch = s.nchunks;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, r16 = lane & 15;
   const int col0 = cg * 16 * kStrips; // first column of this workgroup
 
   __shared__ Stage st[2];
-  // Output tiles of the last two chunks, [token][workgroup column] bf16 with a
-  // row pitch of 32 * kStrips + 16 bytes (16 rows of one column block fall in
-  // distinct banks).  A compute wave writes its strip of chunk c into tile
-  // c % 2; during step c+1 the idle loader pair stores whole row segments of
-  // it; tile c % 2 is next written in step c+2, after the barrier that ends
-  // step c+1.
+  // scores A of chunk c (A operand of A uc, fragment tri_frag(mt, kb)) in
+  // afb[c % 2]: formed in step c, used in step c+1
+  __shared__ u32x4 afb[2][kTpFrags * 64];
+  // Output tiles, [token][workgroup column] bf16 with a row pitch of
+  // 32 * kStrips + 16 bytes (16 rows of one column block fall in distinct
+  // banks): chunk c's tile ost[c % 2] is written in step c+1 and stored in
+  // step c+2.
   constexpr int kOPitch = 32 * kStrips + 16;
   __shared__ __align__(16) char ost[2][kChunk * kOPitch];
 
   // =========================== loader waves ===============================
   if (wave >= kStrips) {
     // Loader li = wave - S is wave 0 of its pair (role 0) for li < 2.  With
-    // waves dealt to the four SIMDs in turn, the two role-0 waves (the heavy
-    // ones) then share no SIMD with a compute wave when S <= 2.
-    const int pair = (wave - kStrips) & 1; // owns chunks c with c % 2 == pair
+    // waves dealt to the four SIMDs in turn, the role-1 waves (the scores)
+    // then share no SIMD with a compute wave when S <= 2.
+    const int pair = (wave - kStrips) & 1; // stages chunks c with c % 2 == pair
     const int role = (wave - kStrips) >> 1;
     const int nrow = lane >> 4, piece = lane & 15; // whole-row loads: 4 rows per instruction
+    // rows of the workgroup's 16 * kStrips columns: 2 * kStrips pieces per row
+    constexpr int kVPieces = 2 * kStrips, kVRows = 64 / kVPieces;
+    const int vpiece = lane % kVPieces, vrow0 = lane / kVPieces;
 
     if (role == 0) {
-      // ---- Q, K rows, and the scores from them --------------------------------
+      // ---- Q, K rows; outputs --------------------------------------------
       u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
-      float gt[4];          // G at t = 16mt + r16
-      f32x4 gs[4];          // G at s = 16ms + 4q .. +3
       auto fetch = [&](int c) {
         const int nn = min(kChunk, s.len - c * kChunk);
         // chunk bases are wave-uniform; a lane adds a 32-bit offset (row
@@ -163,12 +170,6 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
           qx[jr] = *reinterpret_cast<const u32x4 *>(qc + off);
           kx[jr] = *reinterpret_cast<const u32x4 *>(kc + off);
         }
-        const float *gc = p.gc + slot_of(p, s, h, c) * kChunk;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          gt[m] = gc[16 * m + r16];
-          gs[m] = *reinterpret_cast<const f32x4 *>(gc + 16 * m + 4 * q4);
-        }
       };
       auto stash = [&](Stage &S) {
 #pragma unroll
@@ -176,78 +177,44 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
           S.qr[row_slot(4 * jr + nrow, piece)] = qx[jr];
           S.kr[row_slot(4 * jr + nrow, piece)] = kx[jr];
         }
-        // Row fragments are read back from the tiles this wave just wrote, a
-        // few at a time: frag(T, mt, kb) = rows 16mt + r16, columns 32kb + 8q .. +7.
-        auto frag = [&](const u32x4 *T, int mt, int kb) {
-          return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
-        };
-        // C(ms, mt)[s][t] = q_t . k_s: A = K rows s, B = Q rows t; lane holds
-        // column t = 16mt + r16, rows s = 16ms + 4q .. +3.  All Q fragments are
-        // held; each K row tile is read once and used for every mt >= ms.
-        bf16x8 qf[16];
+      };
+      // outputs of chunk co (tile co % 2): whole row segments of the
+      // workgroup's columns
+      const int64_t orow = int64_t(p.nv) * kDim;
+      auto store_out = [&](int co) {
+        const int nn = min(kChunk, s.len - co * kChunk);
+        char *oc = reinterpret_cast<char *>(p.out + (s.tok0 + int64_t(co) * kChunk) * orow + int64_t(h) * kDim + col0);
+        const uint32_t opitch = uint32_t(orow) * 2u;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) qf[4 * mt + kk] = frag(S.qr, mt, kk);
-        f32x4 sc[4][4]; // sc[mt][ms], ms <= mt
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          bf16x8 kf[4];
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) kf[kk] = frag(S.kr, ms, kk);
-#pragma unroll
-          for (int mt = ms; mt < 4; ++mt) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[kk], qf[4 * mt + kk], acc);
-            sc[mt][ms] = acc;
-          }
-        }
-        // masked to s <= t and decayed by exp(G_t - G_s), two vertically
-        // stacked tiles are the chain-order A fragment (mt, kb) of A uc
-        constexpr float kLog2e = 1.4426950408889634f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int t = 16 * mt + r16;
-          const float g2t = gt[mt] * kLog2e;
-#pragma unroll
-          for (int ms = 0; ms <= mt; ++ms)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-              const int si = 16 * ms + 4 * q4 + ii;
-              sc[mt][ms][ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - gs[ms][ii] * kLog2e) * sc[mt][ms][ii] : 0.f;
-            }
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if (2 * kb > mt) continue;
-            const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
-            S.af[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
-          }
+        for (int jj = 0; jj < kVPieces; ++jj) {
+          const int t = vrow0 + jj * kVRows;
+          const u32x4 val = *reinterpret_cast<const u32x4 *>(&ost[co & 1][t * kOPitch + 16 * vpiece]);
+          if (t < nn) *reinterpret_cast<u32x4 *>(oc + uint32_t(t) * opitch + 16u * vpiece) = val;
         }
       };
-      if (pair < s.nchunks) fetch(pair);
+      if (pair < nch) fetch(pair);
       if (pair == 0) {
         stash(st[0]);
-        if (2 < s.nchunks) fetch(2);
+        if (2 < nch) fetch(2);
       }
       __syncthreads();
-      for (int c = 0; c < s.nchunks; ++c) {
-        if (((c + 1) & 1) == pair && c + 1 < s.nchunks) {
+      for (int c = 0; c <= nch; ++c) {
+        if (((c + 1) & 1) == pair && c + 1 < nch) {
           stash(st[(c + 1) & 1]);
-          if (c + 3 < s.nchunks) fetch(c + 3);
+          if (c + 3 < nch) fetch(c + 3);
         }
+        // the idle pair stores the output of chunk c-2
+        if ((c & 1) == pair && c >= 2) store_out(c - 2);
         __syncthreads();
       }
+      // after the last barrier: the last chunk's output
+      if ((nch & 1) == pair) store_out(nch - 1);
       return;
     }
 
-    // ---- T', decays, V rows --------------------------------------------------
+    // ---- T', decays, gate sums, V rows; scores ------------------------------
     u32x4 tx[2 * kTpFrags];
-    float d0 = 0.f, d1 = 0.f;
-    // V rows of the workgroup's 16 * kStrips columns: 2 * kStrips pieces per row,
-    // 32 / kStrips rows per load; vx[jj] = piece vpiece of row vrow0 + jj * vrows
-    constexpr int kVPieces = 2 * kStrips, kVRows = 64 / kVPieces;
-    const int vpiece = lane % kVPieces, vrow0 = lane / kVPieces;
+    float d0 = 0.f, d1 = 0.f, gg = 0.f;
     u32x4 vx[kVPieces];
     auto fetch = [&](int c) {
       const int64_t sl = slot_of(p, s, h, c);
@@ -256,6 +223,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       for (int f = 0; f < 2 * kTpFrags; ++f) tx[f] = tsrc[f * 64 + lane];
       d0 = p.dec[sl * 2 * kChunk + lane];
       d1 = p.dec[sl * 2 * kChunk + kChunk + lane];
+      gg = p.gc[sl * kChunk + lane];
       const int nn = min(kChunk, s.len - c * kChunk);
       const char *vc = reinterpret_cast<const char *>(p.v + (s.tok0 + int64_t(c) * kChunk) * p.v_row + int64_t(h) * kDim + col0);
       const uint32_t pitch = uint32_t(p.v_row) * 2u;
@@ -270,39 +238,73 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       for (int f = 0; f < 2 * kTpFrags; ++f) S.tp[f * 64 + lane] = tx[f];
       S.dec[lane] = d0;
       S.dec[kChunk + lane] = d1;
+      S.g2[lane] = gg * 1.4426950408889634f; // log2(e) G
 #pragma unroll
       for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
-    // outputs of chunk co (staged in tile co % 2): whole row segments of the
-    // workgroup's columns, 2 * kStrips pieces of 16 bytes per token row
-    const int64_t orow = int64_t(p.nv) * kDim;
-    auto store_out = [&](int co) {
-      const int nn = min(kChunk, s.len - co * kChunk);
-      char *oc = reinterpret_cast<char *>(p.out + (s.tok0 + int64_t(co) * kChunk) * orow + int64_t(h) * kDim + col0);
-      const uint32_t opitch = uint32_t(orow) * 2u;
+    // scores of the chunk staged in S, into A: C(ms, mt)[s][t] = q_t . k_s
+    // (A = K rows s, B = Q rows t; lane holds column t = 16mt + r16, rows
+    // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s);
+    // two vertically stacked tiles are the chain-order A fragment (mt, kb)
+    auto scores = [&](const Stage &S, u32x4 *A) {
+      auto frag = [&](const u32x4 *T, int mt, int kb) {
+        return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
+      };
+      bf16x8 qf[16];
 #pragma unroll
-      for (int jj = 0; jj < kVPieces; ++jj) {
-        const int t = vrow0 + jj * kVRows;
-        const u32x4 val = *reinterpret_cast<const u32x4 *>(&ost[co & 1][t * kOPitch + 16 * vpiece]);
-        if (t < nn) *reinterpret_cast<u32x4 *>(oc + uint32_t(t) * opitch + 16u * vpiece) = val;
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[4 * mt + kk] = frag(S.qr, mt, kk);
+      f32x4 sc[4][4]; // sc[mt][ms], ms <= mt
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[kk] = frag(S.kr, ms, kk);
+#pragma unroll
+        for (int mt = ms; mt < 4; ++mt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[kk], qf[4 * mt + kk], acc);
+          sc[mt][ms] = acc;
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int t = 16 * mt + r16;
+        const float g2t = S.g2[t];
+#pragma unroll
+        for (int ms = 0; ms <= mt; ++ms) {
+          const f32x4 g2s = *reinterpret_cast<const f32x4 *>(S.g2 + 16 * ms + 4 * q4);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int si = 16 * ms + 4 * q4 + ii;
+            sc[mt][ms][ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - g2s[ii]) * sc[mt][ms][ii] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (2 * kb > mt) continue;
+          const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
+          A[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
+        }
       }
     };
-    if (pair < s.nchunks) fetch(pair);
+    if (pair < nch) fetch(pair);
     if (pair == 0) {
       stash(st[0]);
-      if (2 < s.nchunks) fetch(2);
+      if (2 < nch) fetch(2);
     }
     __syncthreads();
-    for (int c = 0; c < s.nchunks; ++c) {
-      if (((c + 1) & 1) == pair && c + 1 < s.nchunks) {
+    for (int c = 0; c <= nch; ++c) {
+      if (((c + 1) & 1) == pair && c + 1 < nch) {
         stash(st[(c + 1) & 1]);
-        if (c + 3 < s.nchunks) fetch(c + 3);
+        if (c + 3 < nch) fetch(c + 3);
       }
-      // the idle pair stores the previous chunk's outputs
-      if ((c & 1) == pair && c >= 1) store_out(c - 1);
+      // the idle pair forms the scores of chunk c
+      if ((c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1]);
       __syncthreads();
     }
-    if ((s.nchunks & 1) == pair) store_out(s.nchunks - 1);
     return;
   }
 
@@ -321,60 +323,105 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   asm volatile("" : "+v"(m1));
   const bf16x8 C0 = ident_chain(lane, 0), C1 = ident_chain(lane, 1);
 
-  __syncthreads(); // chunk 0 staged
+  // LDS operand readers: row fragments of the Q / K tiles (rows 16mt + r16,
+  // columns 32kb + 8q .. +7) and K^T fragments (rows dk = perm_dk(16m + r16),
+  // tokens 32kb + chain order: two transposing reads of the K rows)
+  auto rfrag = [&](const u32x4 *T, int mt, int kb) {
+    return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
+  };
+  auto ktfrag = [&](const Stage &S, int m, int kb) {
+    const int pc = 4 * (m >> 1) + (r16 & 3), hb = 8 * (m & 1);
+    const int t0 = 32 * kb + 4 * q4 + (r16 >> 2);
+    const u32x2 lo = read_tr(S.kr, row_slot(t0, pc) * 16 + hb);
+    const u32x2 hi = read_tr(S.kr, row_slot(t0 + 16, pc) * 16 + hb);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  // interleave, in the current scheduling region, n MFMAs each followed by v
+  // vector instructions
+#define GDN_INTERLEAVE(n, v, id)                                                                                       \
+  do {                                                                                                                 \
+    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {                                                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, id);                                                              \
+      __builtin_amdgcn_sched_group_barrier(0x002, v, id);                                                              \
+    }                                                                                                                  \
+  } while (0)
 
-  for (int c = 0; c < s.nchunks; ++c) {
-    const Stage &S = st[c & 1];
-    const int64_t sl = slot_of(p, s, h, c);
-
-    // h -> hi/lo bf16, chain order over dk (a lane's eight values are dk
-    // 32kb + 8q .. +7); bf16(h) is also the entry state
-    bf16x8 Hh[4], Hl[4];
+  // chunk c-1's output, finished in step c: O += A uc, bf16, turned by an
+  // identity product so a lane holds 4 consecutive columns of one token, into
+  // the chunk's output tile
+  f32x4 O[4];      // diag(exp(G)) Q h of the chunk whose output is pending
+  bf16x8 ub[2];    // its bf16(uc), chain order over tokens
+  auto finish_output = [&](int co) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) split_tiles(H[2 * kb], H[2 * kb + 1], m0, m1, Hh[kb], Hl[kb]);
-    {
-      // S_c = h^T: row dv = colw + r16, dk = 32kb + 8q .. +7
-      uint16_t *sdst = p.s_entry + sl * (kDim * kDim) + (colw + r16) * kDim + 8 * q4;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<u32x4 *>(sdst + 32 * kb) = __builtin_bit_cast(u32x4, Hh[kb]);
-    }
-
-    // K h  (C tile mt: column colw + r16, rows t = 16mt + 4q .. +3); the row
-    // fragments of block kb+1 are in flight while block kb's products issue
-    auto kfrag = [&](const u32x4 *T, int mt, int kb) {
-      return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
-    };
-    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-    {
-      bf16x8 ka[2][4];
+      for (int mt = 2 * kb; mt < 4; ++mt)
+        O[mt] = mfma(__builtin_bit_cast(bf16x8, afb[co & 1][tri_frag(mt, kb) * 64 + lane]), ub[kb], O[mt]);
+    char *ot = &ost[co & 1][32 * wave + 8 * q4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) ka[0][mt] = kfrag(S.kr, mt, 0);
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 oa = chain_frag(O[2 * kk], O[2 * kk + 1]);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb < 3) {
-          // with few compute waves per CU, read block kb+1 before block kb's
-          // products (latency hidden); with four, read it after them (fewer
-          // reads in flight at once on the shared LDS)
-          if constexpr (kAhead) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) ka[(kb + 1) & 1][mt] = kfrag(S.kr, mt, kb + 1);
-          }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[kb & 1][mt], Hh[kb], acc[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma(ka[kb & 1][mt], Hl[kb], acc[mt]);
-        if constexpr (!kAhead) {
-          if (kb < 3) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) ka[(kb + 1) & 1][mt] = kfrag(S.kr, mt, kb + 1);
-          }
-        }
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 d = mfma(oa, hf ? C1 : C0, zero4());
+        const int t = 32 * kk + 16 * hf + r16;
+        *reinterpret_cast<u32x2 *>(ot + t * kOPitch) = pack4_bf16(d[0], d[1], d[2], d[3]);
       }
     }
+  };
 
-    // R = V - diag(exp(G)) K h, split; the output's state term Q h (bf16 h)
-    // is off the dependent chain and issues among R's vector instructions
+  __syncthreads(); // chunk 0 staged
+
+  // One chunk step.  The dependent chain is  split(h) -> K h -> R -> split ->
+  // T' R -> uc -> split -> K^T uc -> h.  T' is lower triangular, so rows 0..31
+  // of uc (half A) need rows 0..31 of R only: the step runs as two halves, the
+  // vector work of one half issuing while the MFMAs of the other run, and the
+  // output's products (the previous chunk's A uc, this chunk's Q h) filling
+  // the split of h.  Scheduling barriers keep the sections in this order.
+  for (int c = 0; c < nch; ++c) {
+    const Stage &S = st[c & 1];
+    const int64_t sl = slot_of(p, s, h, c);
+    uint16_t *sdst = p.s_entry + sl * (kDim * kDim) + (colw + r16) * kDim + 8 * q4;
+
+    // ---- h -> hi/lo (chain order over dk, eight consecutive dk per lane);
+    // bf16(h) is the entry state.  The previous chunk's output, then Q h, the
+    // output's state term, issue among the split's vector instructions.
+    bf16x8 Hh[4], Hl[4];
+    bf16x8 kA[4][2], qa[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) kA[kb][mt] = rfrag(S.kr, mt, kb);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) qa[0][mt] = rfrag(S.qr, mt, 0);
+    if (c > 0) finish_output(c - 1);
+    split_tiles(H[0], H[1], m0, m1, Hh[0], Hl[0]);
+    *reinterpret_cast<u32x4 *>(sdst) = __builtin_bit_cast(u32x4, Hh[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) O[mt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < 3) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) qa[(kb + 1) & 1][mt] = rfrag(S.qr, mt, kb + 1);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(qa[kb & 1][mt], Hh[kb], O[mt]);
+      if (kb < 3) {
+        split_tiles(H[2 * kb + 2], H[2 * kb + 3], m0, m1, Hh[kb + 1], Hl[kb + 1]);
+        *reinterpret_cast<u32x4 *>(sdst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
+        GDN_INTERLEAVE(4, 5, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- K h, half A (rows 0..31), while h is scaled by exp(G_n) ----------
+    bf16x8 kB[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) kB[kb][mt] = rfrag(S.kr, mt + 2, kb);
     f32x4 eg[4];
     u32x2 vv[4];
 #pragma unroll
@@ -383,152 +430,121 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       // V[16mt + 4q + ii][colw + r16], ii = 0..3: a transposing read of the V rows
       vv[mt] = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
     }
-    bf16x8 qa[16];
+    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) qa[4 * kb + mt] = kfrag(S.qr, mt, kb);
-    f32x4 R[4];
+      for (int mt = 0; mt < 2; ++mt) {
+        acc[mt] = mfma(kA[kb][mt], Hh[kb], acc[mt]);
+        acc[mt] = mfma(kA[kb][mt], Hl[kb], acc[mt]);
+      }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int m = 0; m < 8; ++m) H[m] *= en;
+    GDN_INTERLEAVE(16, 2, 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- K h, half B, while R = V - diag(exp(G)) K h of half A is formed ---
+    bf16x8 th[kTpFrags], tl[kTpFrags];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      th[tri_frag(mt, 0)] = __builtin_bit_cast(bf16x8, S.tp[tri_frag(mt, 0) * 64 + lane]);
+      tl[tri_frag(mt, 0)] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + tri_frag(mt, 0)) * 64 + lane]);
+    }
+    auto form_r = [&](int mt, f32x4 &R) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const uint32_t pr = vv[mt][ii >> 1];
         const float v = __builtin_bit_cast(float, (ii & 1) ? (pr & 0xFFFF0000u) : (pr << 16));
-        R[mt][ii] = v - eg[mt][ii] * acc[mt][ii];
+        R[ii] = v - eg[mt][ii] * acc[mt][ii];
       }
-    f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+    };
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(qa[4 * kb + mt], Hh[kb], O[mt]);
-    bf16x8 Rh[2], Rl[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) split_tiles(R[2 * kb], R[2 * kb + 1], m0, m1, Rh[kb], Rl[kb]);
-    if constexpr (kAhead) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // then four VALU
+      for (int mt = 0; mt < 2; ++mt) {
+        acc[mt + 2] = mfma(kB[kb][mt], Hh[kb], acc[mt + 2]);
+        acc[mt + 2] = mfma(kB[kb][mt], Hl[kb], acc[mt + 2]);
       }
-    }
+    f32x4 R[4];
+    form_r(0, R[0]);
+    form_r(1, R[1]);
+    bf16x8 Rh[2], Rl[2];
+    split_tiles(R[0], R[1], m0, m1, Rh[0], Rl[0]);
+    GDN_INTERLEAVE(16, 3, 2);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // uc = T' R  (T' is lower triangular: fragment (mt, 1) is zero for mt < 2);
-    // all T' fragments are read up front
-    bf16x8 th[kTpFrags], tl[kTpFrags];
-    auto tpfrag = [&](int f) {
-      th[f] = __builtin_bit_cast(bf16x8, S.tp[f * 64 + lane]);
-      tl[f] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + f) * 64 + lane]);
-    };
-    if constexpr (kAhead) {
+    // ---- uc = T' R: half A (rows 0..31) and the R-A part of half B, while R
+    // of half B is formed ----------------------------------------------------
 #pragma unroll
-      for (int f = 0; f < kTpFrags; ++f) tpfrag(f);
+    for (int mt = 2; mt < 4; ++mt) {
+      th[tri_frag(mt, 1)] = __builtin_bit_cast(bf16x8, S.tp[tri_frag(mt, 1) * 64 + lane]);
+      tl[tri_frag(mt, 1)] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + tri_frag(mt, 1)) * 64 + lane]);
     }
     f32x4 D[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (!kAhead) {
-#pragma unroll
-        for (int mt = 2 * kb; mt < 4; ++mt) tpfrag(tri_frag(mt, kb));
-      }
-#pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[tri_frag(mt, kb)], Rh[kb], D[mt]);
-#pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(th[tri_frag(mt, kb)], Rl[kb], D[mt]);
-#pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) D[mt] = mfma(tl[tri_frag(mt, kb)], Rh[kb], D[mt]);
+    for (int mt = 0; mt < 4; ++mt) {
+      D[mt] = mfma(th[tri_frag(mt, 0)], Rh[0], D[mt]);
+      D[mt] = mfma(th[tri_frag(mt, 0)], Rl[0], D[mt]);
+      D[mt] = mfma(tl[tri_frag(mt, 0)], Rh[0], D[mt]);
     }
-    bf16x8 af[kTpFrags];
-    if constexpr (kAhead) {
-#pragma unroll
-      for (int f = 0; f < kTpFrags; ++f) af[f] = __builtin_bit_cast(bf16x8, S.af[f * 64 + lane]);
-    }
-    // K^T fragment (m, kb): row dk = perm_dk(16m + r16), tokens 32kb + chain
-    // order -- two transposing reads of the K rows
-    auto ktfrag = [&](int m, int kb) {
-      const int pc = 4 * (m >> 1) + (r16 & 3), hb = 8 * (m & 1);
-      const int t0 = 32 * kb + 4 * q4 + (r16 >> 2);
-      const u32x2 lo = read_tr(S.kr, row_slot(t0, pc) * 16 + hb);
-      const u32x2 hi = read_tr(S.kr, row_slot(t0 + 16, pc) * 16 + hb);
-      return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    };
-    bf16x8 ka[2][8];
-    if constexpr (kAhead) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) ka[0][m] = ktfrag(m, 0);
-    }
+    form_r(2, R[2]);
+    form_r(3, R[3]);
+    split_tiles(R[2], R[3], m0, m1, Rh[1], Rl[1]);
+    GDN_INTERLEAVE(12, 3, 3);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // h <- exp(G_n) h + K^T diag(exp(G_n - G)) uc; the output's intra-chunk
-    // term A bf16(uc) issues among the vector instructions of the split
-    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
-    bf16x8 ub[2];
+    // ---- uc half B (R-B part), while half A of uc is rounded for the output,
+    // decayed and split; the output's state term is scaled ------------------
+    bf16x8 kt0[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) ub[kb] = chain_frag(D[2 * kb], D[2 * kb + 1]);
+    for (int m = 0; m < 8; ++m) kt0[m] = ktfrag(S, m, 0);
+#pragma unroll
+    for (int mt = 2; mt < 4; ++mt) {
+      D[mt] = mfma(th[tri_frag(mt, 1)], Rh[1], D[mt]);
+      D[mt] = mfma(th[tri_frag(mt, 1)], Rl[1], D[mt]);
+      D[mt] = mfma(tl[tri_frag(mt, 1)], Rh[1], D[mt]);
+    }
+    bf16x8 Dh[2], Dl[2];
+    ub[0] = chain_frag(D[0], D[1]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) D[mt] *= *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
+    split_tiles(D[0], D[1], m0, m1, Dh[0], Dl[0]);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) O[mt] *= eg[mt];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt) {
-        if constexpr (!kAhead) af[tri_frag(mt, kb)] = __builtin_bit_cast(bf16x8, S.af[tri_frag(mt, kb) * 64 + lane]);
-        O[mt] = mfma(af[tri_frag(mt, kb)], ub[kb], O[mt]);
-      }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) H[m] *= en;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) D[mt] *= *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
-    bf16x8 Dh[2], Dl[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) split_tiles(D[2 * kb], D[2 * kb + 1], m0, m1, Dh[kb], Dl[kb]);
-    if constexpr (kAhead) {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1); // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1); // then six VALU
-      }
-    }
-    if constexpr (!kAhead) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) ka[0][m] = ktfrag(m, 0);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (kAhead) {
-        if (kb == 0) {
-#pragma unroll
-          for (int m = 0; m < 8; ++m) ka[1][m] = ktfrag(m, 1);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[kb][m], Dh[kb], H[m]);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) H[m] = mfma(ka[kb][m], Dl[kb], H[m]);
-      if constexpr (!kAhead) {
-        if (kb == 0) {
-#pragma unroll
-          for (int m = 0; m < 8; ++m) ka[1][m] = ktfrag(m, 1);
-        }
-      }
-    }
+    GDN_INTERLEAVE(6, 6, 4);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // output: bf16, turned by an identity product so a lane holds 4
-    // consecutive columns of one token, into this chunk's output tile
-    {
-      char *ot = &ost[c & 1][32 * wave + 8 * q4];
+    // ---- h += K^T diag(exp(G_n - G)) uc, half A, while half B of uc is
+    // rounded, decayed and split --------------------------------------------
+    bf16x8 kt1[8];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 oa = chain_frag(O[2 * kk], O[2 * kk + 1]);
+    for (int m = 0; m < 8; ++m) kt1[m] = ktfrag(S, m, 1);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 d = mfma(oa, hf ? C1 : C0, zero4());
-          const int t = 32 * kk + 16 * hf + r16;
-          *reinterpret_cast<u32x2 *>(ot + t * kOPitch) = pack4_bf16(d[0], d[1], d[2], d[3]);
-        }
-      }
+    for (int m = 0; m < 8; ++m) {
+      H[m] = mfma(kt0[m], Dh[0], H[m]);
+      H[m] = mfma(kt0[m], Dl[0], H[m]);
+    }
+    ub[1] = chain_frag(D[2], D[3]);
+#pragma unroll
+    for (int mt = 2; mt < 4; ++mt) D[mt] *= *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
+    split_tiles(D[2], D[3], m0, m1, Dh[1], Dl[1]);
+    GDN_INTERLEAVE(16, 2, 5);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- h += ..., half B --------------------------------------------------
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      H[m] = mfma(kt1[m], Dh[1], H[m]);
+      H[m] = mfma(kt1[m], Dl[1], H[m]);
     }
 
     __syncthreads();
   }
+  // the last chunk's output: its scores were formed in the last step
+  finish_output(nch - 1);
+  __syncthreads();
+#undef GDN_INTERLEAVE
 
 #pragma unroll
   for (int m = 0; m < 8; ++m)
