@@ -55,17 +55,26 @@
 namespace gdn {
 
 // Q and K tiles are kept as rows: 64 rows of 16 pieces of 16 bytes, piece p of
-// row t at slot 16t + (p ^ sig(t % 16)), sig swapping the two bit pairs of a
-// 4-bit row index.  Without bank conflicts, 16 lanes then write a whole row,
-// read a row fragment (16 rows, one piece each), or read with the transposing
-// load a 4 x 4 block of 8-byte half pieces (rows t0..t0+3, pieces p0..p0+3,
-// t0 and p0 multiples of 4).
+// row t at slot 16t + (p ^ swz(t % 16)), swz moving the bits (t0, t1, t2, t3)
+// of the row index to bits (0, 2, 3, 1).  gfx950's LDS serves a 16-byte read
+// in four passes of 16 lanes, lanes 0..31 split by the parity of bits 2..4 of
+// the lane id (likewise 32..63), and a pass is free of bank conflicts when
+// its 16 lanes touch 16 distinct 16-byte columns of the 256-byte bank row;
+// 8-byte reads take passes of 32 consecutive lanes, 16-byte writes passes of
+// 8 consecutive lanes over 128 bytes.  With swz, 16 lanes write a whole row,
+// and a row fragment (16 rows, one piece each) is read, without conflicts;
+// the transposing read of a 4 x 4 block of 8-byte half pieces (rows t0..t0+3,
+// pieces p0..p0+3, t0 and p0 multiples of 4) meets each bank twice (its 32
+// lanes read one half of each piece).
 __device__ __forceinline__ int row_slot(int t, int piece) {
-  return 16 * t + (piece ^ (((t & 3) << 2) | ((t >> 2) & 3)));
+  const int swz = (t & 1) | ((t & 2) << 1) | ((t & 4) << 1) | ((t & 8) >> 2);
+  return 16 * t + (piece ^ swz);
 }
-// The V tile: 64 rows of (up to) 8 pieces, the workgroup's 64 columns; piece p
-// of row t at slot 8t + (p ^ (2 * ((t >> 1) & 1))).
-__device__ __forceinline__ int vrow_slot(int t, int piece) { return 8 * t + (piece ^ (2 * ((t >> 1) & 1))); }
+// The V tile: 64 rows of (up to) 8 pieces, the workgroup's columns; piece p of
+// row t at slot 8t + (p ^ vswz(t)), vswz(t) = 2 ((t / 2) % 4) ^ 4 (t % 2): the
+// transposing read of 8 rows x 2 pieces and the row writes (8 lanes over 1,
+// 2 or 4 rows) meet each bank once.
+__device__ __forceinline__ int vrow_slot(int t, int piece) { return 8 * t + (piece ^ ((2 * ((t >> 1) & 3)) ^ (4 * (t & 1)))); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -321,7 +330,6 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   uint32_t m0 = 0x0000BF80u, m1 = 0xBF800000u;
   asm volatile("" : "+v"(m0));
   asm volatile("" : "+v"(m1));
-  const bf16x8 C0 = ident_chain(lane, 0), C1 = ident_chain(lane, 1);
 
   // LDS operand readers: row fragments of the Q / K tiles (rows 16mt + r16,
   // columns 32kb + 8q .. +7) and K^T fragments (rows dk = perm_dk(16m + r16),
@@ -346,28 +354,28 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     }                                                                                                                  \
   } while (0)
 
-  // chunk c-1's output, finished in step c: O += A uc, bf16, turned by an
-  // identity product so a lane holds 4 consecutive columns of one token, into
-  // the chunk's output tile
-  f32x4 O[4];      // diag(exp(G)) Q h of the chunk whose output is pending
+  // The output is formed transposed, O^T = h^T Q^T + uc^T A^T, so that tile mt
+  // holds, in lane (q, r), token 16mt + r and the four columns colw + 4q .. +3:
+  // the split of h (chain order over dk) is the A operand of h^T Q^T as it is
+  // the B operand of K h, and likewise bf16(uc) for uc^T A^T; the Q and score
+  // fragments serve as B operands unchanged.
+  f32x4 O[4];      // O^T of the chunk whose output is pending: diag(exp(G)) Q h so far
   bf16x8 ub[2];    // its bf16(uc), chain order over tokens
-  auto finish_output = [&](int co) {
+  // chunk c-1's output, finished in step c from the score fragments af: O^T +=
+  // uc^T A^T, then bf16 into the chunk's output tile (8 bytes per lane per tile)
+  auto finish_output = [&](int co, const bf16x8 (&af)[kTpFrags]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int mt = 2 * kb; mt < 4; ++mt)
-        O[mt] = mfma(__builtin_bit_cast(bf16x8, afb[co & 1][tri_frag(mt, kb) * 64 + lane]), ub[kb], O[mt]);
+      for (int mt = 2 * kb; mt < 4; ++mt) O[mt] = mfma(ub[kb], af[tri_frag(mt, kb)], O[mt]);
     char *ot = &ost[co & 1][32 * wave + 8 * q4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 oa = chain_frag(O[2 * kk], O[2 * kk + 1]);
+    for (int mt = 0; mt < 4; ++mt)
+      *reinterpret_cast<u32x2 *>(ot + (16 * mt + r16) * kOPitch) = pack4_bf16(O[mt][0], O[mt][1], O[mt][2], O[mt][3]);
+  };
+  auto load_scores = [&](int co, bf16x8 (&af)[kTpFrags]) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 d = mfma(oa, hf ? C1 : C0, zero4());
-        const int t = 32 * kk + 16 * hf + r16;
-        *reinterpret_cast<u32x2 *>(ot + t * kOPitch) = pack4_bf16(d[0], d[1], d[2], d[3]);
-      }
-    }
+    for (int f = 0; f < kTpFrags; ++f) af[f] = __builtin_bit_cast(bf16x8, afb[co & 1][f * 64 + lane]);
   };
 
   __syncthreads(); // chunk 0 staged
@@ -394,7 +402,12 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       for (int mt = 0; mt < 2; ++mt) kA[kb][mt] = rfrag(S.kr, mt, kb);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) qa[0][mt] = rfrag(S.qr, mt, 0);
-    if (c > 0) finish_output(c - 1);
+    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
+    if (c > 0) {
+      bf16x8 af[kTpFrags];
+      load_scores(c - 1, af);
+      finish_output(c - 1, af);
+    }
     split_tiles(H[0], H[1], m0, m1, Hh[0], Hl[0]);
     *reinterpret_cast<u32x4 *>(sdst) = __builtin_bit_cast(u32x4, Hh[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -407,7 +420,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         for (int mt = 0; mt < 4; ++mt) qa[(kb + 1) & 1][mt] = rfrag(S.qr, mt, kb + 1);
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(qa[kb & 1][mt], Hh[kb], O[mt]);
+      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(Hh[kb], qa[kb & 1][mt], O[mt]);
       if (kb < 3) {
         split_tiles(H[2 * kb + 2], H[2 * kb + 3], m0, m1, Hh[kb + 1], Hl[kb + 1]);
         *reinterpret_cast<u32x4 *>(sdst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
@@ -430,7 +443,6 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       // V[16mt + 4q + ii][colw + r16], ii = 0..3: a transposing read of the V rows
       vv[mt] = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
     }
-    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -511,7 +523,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     for (int mt = 0; mt < 2; ++mt) D[mt] *= *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
     split_tiles(D[0], D[1], m0, m1, Dh[0], Dl[0]);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) O[mt] *= eg[mt];
+    for (int mt = 0; mt < 4; ++mt) O[mt] *= S.dec[16 * mt + r16];
     GDN_INTERLEAVE(6, 6, 4);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -542,7 +554,11 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     __syncthreads();
   }
   // the last chunk's output: its scores were formed in the last step
-  finish_output(nch - 1);
+  {
+    bf16x8 af[kTpFrags];
+    load_scores(nch - 1, af);
+    finish_output(nch - 1, af);
+  }
   __syncthreads();
 #undef GDN_INTERLEAVE
 
