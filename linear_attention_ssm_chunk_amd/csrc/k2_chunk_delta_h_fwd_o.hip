@@ -408,6 +408,11 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       load_scores(c - 1, af);
       finish_output(c - 1, af);
     }
+    // exp(G_n) h goes to new registers before each pair is split, so that the
+    // split can overwrite h in place
+    f32x4 Hn[8];
+    Hn[0] = H[0] * en;
+    Hn[1] = H[1] * en;
     split_tiles(H[0], H[1], m0, m1, Hh[0], Hl[0]);
     *reinterpret_cast<u32x4 *>(sdst) = __builtin_bit_cast(u32x4, Hh[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -422,6 +427,8 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(Hh[kb], qa[kb & 1][mt], O[mt]);
       if (kb < 3) {
+        Hn[2 * kb + 2] = H[2 * kb + 2] * en;
+        Hn[2 * kb + 3] = H[2 * kb + 3] * en;
         split_tiles(H[2 * kb + 2], H[2 * kb + 3], m0, m1, Hh[kb + 1], Hl[kb + 1]);
         *reinterpret_cast<u32x4 *>(sdst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
         GDN_INTERLEAVE(4, 5, 0);
@@ -451,8 +458,6 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         acc[mt] = mfma(kA[kb][mt], Hh[kb], acc[mt]);
         acc[mt] = mfma(kA[kb][mt], Hl[kb], acc[mt]);
       }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) H[m] *= en;
     GDN_INTERLEAVE(16, 2, 1);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -534,8 +539,8 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     for (int m = 0; m < 8; ++m) kt1[m] = ktfrag(S, m, 1);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      H[m] = mfma(kt0[m], Dh[0], H[m]);
-      H[m] = mfma(kt0[m], Dl[0], H[m]);
+      Hn[m] = mfma(kt0[m], Dh[0], Hn[m]);
+      Hn[m] = mfma(kt0[m], Dl[0], Hn[m]);
     }
     ub[1] = chain_frag(D[2], D[3]);
 #pragma unroll
@@ -547,9 +552,11 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     // ---- h += ..., half B --------------------------------------------------
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      H[m] = mfma(kt1[m], Dh[1], H[m]);
-      H[m] = mfma(kt1[m], Dl[1], H[m]);
+      Hn[m] = mfma(kt1[m], Dh[1], Hn[m]);
+      Hn[m] = mfma(kt1[m], Dl[1], Hn[m]);
     }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) H[m] = Hn[m];
 
     __syncthreads();
   }

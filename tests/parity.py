@@ -12,6 +12,8 @@ Tolerances (written here once, used by every parity test):
     oracle's direct triangular solves
 """
 
+import os
+
 import numpy as np
 
 from oracle import gdn_chunked, gdn_recurrence, kv_head_map
@@ -137,6 +139,8 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
 
 
 def assert_within(worst, intermediates=False, entries=True):
+    if os.environ.get("GDN_PARITY_VERBOSE"):
+        print("worst errors:", {k: float("%.3g" % v) for k, v in worst.items()}, flush=True)
     assert worst["o_maxabs"] <= TOL_O_MAXABS, worst
     assert worst["state_relfro"] <= TOL_STATE_RELFRO, worst
     if entries:
