@@ -86,6 +86,10 @@ __device__ __forceinline__ u32x2 read_tr(const void *lds_base, int byte_off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a));
 }
 
+template <int N> struct Mask {
+  static constexpr int value = N;
+};
+
 struct Stage {
   u32x4 kr[64 * 16];          // K rows: row fragments for K h and the scores, K^T for K^T uc
   u32x4 qr[64 * 16];          // Q rows: row fragments for Q h and the scores
@@ -150,16 +154,73 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 
   // =========================== loader waves ===============================
   if (wave >= kStrips) {
-    // Loader li = wave - S is wave 0 of its pair (role 0) for li < 2.  With
-    // waves dealt to the four SIMDs in turn, the role-1 waves (the scores)
-    // then share no SIMD with a compute wave when S <= 2.
+    // Loader li = wave - S belongs to pair li % 2.  Waves are dealt to the four
+    // SIMDs in turn, so for S <= 2 loaders li = 0, 1 sit on SIMDs without a
+    // compute wave: they take role 1 (with the score products), and the light
+    // role 0 shares a SIMD with a compute wave.  For S = 4 every SIMD holds one
+    // compute wave and one loader.
     const int pair = (wave - kStrips) & 1; // stages chunks c with c % 2 == pair
-    const int role = (wave - kStrips) >> 1;
+    const int role = (kStrips <= 2) ? 1 - ((wave - kStrips) >> 1) : ((wave - kStrips) >> 1);
     const int nrow = lane >> 4, piece = lane & 15; // whole-row loads: 4 rows per instruction
     // rows of the workgroup's 16 * kStrips columns: 2 * kStrips pieces per row
     constexpr int kVPieces = 2 * kStrips, kVRows = 64 / kVPieces;
     const int vpiece = lane % kVPieces, vrow0 = lane / kVPieces;
 
+  // scores of the chunk staged in S, into A: C(ms, mt)[s][t] = q_t . k_s
+  // (A = K rows s, B = Q rows t; lane holds column t = 16mt + r16, rows
+  // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s);
+  // two vertically stacked tiles are the chain-order A fragment (mt, kb)
+  // The fragments of the row blocks mt in the bit mask are formed (the
+  // caller passes Mask<bits>).
+  auto scores = [&](const Stage &S, u32x4 *A, auto mask_tag) {
+    constexpr int mask = decltype(mask_tag)::value;
+    constexpr int top = (mask & 8) ? 3 : (mask & 4) ? 2 : (mask & 2) ? 1 : 0;
+    auto frag = [&](const u32x4 *T, int mt, int kb) {
+      return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
+    };
+    bf16x8 qf[16];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (mask & (1 << mt)) qf[4 * mt + kk] = frag(S.qr, mt, kk);
+    f32x4 sc[4][4]; // sc[mt][ms], ms <= mt
+#pragma unroll
+    for (int ms = 0; ms <= top; ++ms) {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[kk] = frag(S.kr, ms, kk);
+#pragma unroll
+      for (int mt = ms; mt < 4; ++mt) {
+        if (!(mask & (1 << mt))) continue;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[kk], qf[4 * mt + kk], acc);
+        sc[mt][ms] = acc;
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (!(mask & (1 << mt))) continue;
+      const int t = 16 * mt + r16;
+      const float g2t = S.g2[t];
+#pragma unroll
+      for (int ms = 0; ms <= mt; ++ms) {
+        const f32x4 g2s = *reinterpret_cast<const f32x4 *>(S.g2 + 16 * ms + 4 * q4);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int si = 16 * ms + 4 * q4 + ii;
+          sc[mt][ms][ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - g2s[ii]) * sc[mt][ms][ii] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (2 * kb > mt) continue;
+        const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
+        A[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
+      }
+    }
+  };
     if (role == 0) {
       // ---- Q, K rows; outputs --------------------------------------------
       u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
@@ -212,8 +273,10 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
           stash(st[(c + 1) & 1]);
           if (c + 3 < nch) fetch(c + 3);
         }
-        // the idle pair stores the output of chunk c-2
+        // the idle pair stores the output of chunk c-2 and, for S = 4, forms
+        // half of chunk c's scores
         if ((c & 1) == pair && c >= 2) store_out(c - 2);
+        if (kStrips == 4 && (c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<0x9>());
         __syncthreads();
       }
       // after the last barrier: the last chunk's output
@@ -251,54 +314,6 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
       for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
-    // scores of the chunk staged in S, into A: C(ms, mt)[s][t] = q_t . k_s
-    // (A = K rows s, B = Q rows t; lane holds column t = 16mt + r16, rows
-    // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s);
-    // two vertically stacked tiles are the chain-order A fragment (mt, kb)
-    auto scores = [&](const Stage &S, u32x4 *A) {
-      auto frag = [&](const u32x4 *T, int mt, int kb) {
-        return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
-      };
-      bf16x8 qf[16];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[4 * mt + kk] = frag(S.qr, mt, kk);
-      f32x4 sc[4][4]; // sc[mt][ms], ms <= mt
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        bf16x8 kf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kf[kk] = frag(S.kr, ms, kk);
-#pragma unroll
-        for (int mt = ms; mt < 4; ++mt) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[kk], qf[4 * mt + kk], acc);
-          sc[mt][ms] = acc;
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int t = 16 * mt + r16;
-        const float g2t = S.g2[t];
-#pragma unroll
-        for (int ms = 0; ms <= mt; ++ms) {
-          const f32x4 g2s = *reinterpret_cast<const f32x4 *>(S.g2 + 16 * ms + 4 * q4);
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int si = 16 * ms + 4 * q4 + ii;
-            sc[mt][ms][ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - g2s[ii]) * sc[mt][ms][ii] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (2 * kb > mt) continue;
-          const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
-          A[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
-        }
-      }
-    };
     if (pair < nch) fetch(pair);
     if (pair == 0) {
       stash(st[0]);
@@ -310,8 +325,8 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         stash(st[(c + 1) & 1]);
         if (c + 3 < nch) fetch(c + 3);
       }
-      // the idle pair forms the scores of chunk c
-      if ((c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1]);
+      // the idle pair forms the scores of chunk c (with role 0 for S = 4)
+      if ((c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<kStrips == 4 ? 0x6 : 0xF>());
       __syncthreads();
     }
     return;
