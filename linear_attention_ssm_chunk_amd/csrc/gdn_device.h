@@ -90,26 +90,6 @@ __device__ __forceinline__ void chain_split(const f32x4 &t0, const f32x4 &t1, bf
   split8(x, hi, lo);
 }
 
-// Identity operands.  B-side identity selecting k = 16*half + column under the
-// contiguous k order, and under the chain k order.
-__device__ __forceinline__ bf16x8 ident_contig(int lane, int half) {
-  const int q = lane >> 4, r = lane & 15;
-  bf16x8 f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = to_bf16((8 * q + e == 16 * half + r) ? 1.f : 0.f);
-  return f;
-}
-__device__ __forceinline__ bf16x8 ident_chain(int lane, int half) {
-  const int q = lane >> 4, r = lane & 15;
-  bf16x8 f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int kk = (e < 4) ? 4 * q + e : 16 + 4 * q + (e - 4);
-    f[e] = to_bf16((kk == 16 * half + r) ? 1.f : 0.f);
-  }
-  return f;
-}
-
 // The dk order of the spine.  Row rho = 16m + 4q + i of the state tiles
 // (m = 0..7, q, i = 0..3) holds dk = perm_dk(rho) = 32(m/2) + 8q + 4(m%2) + i.
 // Then the chain fragment of tiles (2kb, 2kb+1) gives a lane eight consecutive
@@ -117,17 +97,6 @@ __device__ __forceinline__ bf16x8 ident_chain(int lane, int half) {
 // 16-byte pieces, and the contiguous k order of a row fragment is this order.
 __host__ __device__ constexpr int perm_dk(int rho) {
   return 32 * (rho >> 5) + 8 * ((rho >> 2) & 3) + 4 * ((rho >> 4) & 1) + (rho & 3);
-}
-
-// B operand that turns a row fragment (contiguous k order) into the columns
-// perm_dk(16*half + j), j = 0..15, of its 32-wide k block: the product's C
-// tile holds, at column j, the row element of dk perm_dk(16*half + j).
-__device__ __forceinline__ bf16x8 ident_perm(int lane, int half) {
-  const int q = lane >> 4, j = lane & 15;
-  bf16x8 f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = to_bf16((8 * q + e == perm_dk(16 * half + j)) ? 1.f : 0.f);
-  return f;
 }
 
 // Fragment slot of a lower-triangular 64x64 A operand (T', the scores) held as
