@@ -15,7 +15,7 @@
 // One wave per (chunk, v-head):
 //   * lane t scans g; emits gc, exp(G_t) and exp(G_{n-1} - G_t);
 //   * the lower 10 tiles of K K^T on bf16 MFMA (K is exact in bf16) -> L (f32,
-//     LDS, its three lower 32x32 blocks only: 14 KB, so that 11 workgroups
+//     LDS, its three lower 32x32 blocks only: 12.8 KB, so that 12 workgroups
 //     fit a CU);
 //   * the two diagonal 32x32 blocks of T = (I+L)^-1 by f32 forward
 //     substitution, one lane per column (32 rows, <= 496 FMAs per lane);
@@ -28,7 +28,7 @@
 
 namespace gdn {
 
-constexpr int kBP = 36; // pitch (floats) of the 32x32 L / T blocks
+constexpr int kBP = 32; // pitch (floats) of the 32x32 L / T blocks (12.8 KB of LDS: 12 workgroups per CU)
 
 __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
   // Workgroup order: all nv heads of one chunk get ids 8 apart, so that on a
