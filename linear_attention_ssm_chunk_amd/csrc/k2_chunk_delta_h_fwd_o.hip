@@ -27,17 +27,19 @@
 //   * waves S..S+3 (loaders), two pairs that take turns.  In step c the
 //     active pair stages chunk c+1 into the free half of a double-buffered
 //     LDS stage, from registers it filled two steps earlier, then fetches
-//     chunk c+3: wave 0 the Q and K rows (1 KB per load), wave 1 the T'
+//     chunk c+3: role 0 the Q and K rows (1 KB per load), role 1 the T'
 //     fragments, decays, gate sums and V rows.  The idle pair works on chunk
-//     c, visible in the stage compute reads: wave 1 reads back the Q and K
-//     row fragments and forms the causal decayed scores A of chunk c on MFMA;
-//     wave 0 stores the output tile of chunk c-2.
+//     c, visible in the stage compute reads: role 1 reads the Q and K row
+//     fragments and forms the causal decayed scores A of chunk c on MFMA
+//     (for S = 4 role 0 forms half of them); role 0 stores the output tile of
+//     chunk c-2.
 //     The compute waves read K^T and their V tiles out of the row tiles with
 //     transposing LDS reads.
 // One barrier per chunk (and one after the last).  Entry states leave as
-// 16-byte pieces (dk order perm_dk).  Outputs are turned by an identity
-// product into 8-byte pieces of token rows, gathered per chunk in an LDS tile,
-// and stored by a loader as whole row segments of the workgroup's columns.
+// 16-byte pieces (dk order perm_dk).  The output is formed transposed, so a
+// lane holds 8-byte pieces of token rows; they are gathered per chunk in an
+// LDS tile and stored by a loader as whole row segments of the workgroup's
+// columns.
 // Every double-buffered region (stage, scores, output tile) is written in one
 // step and read in the next, and written again only after the barrier that
 // ends the reading step.
@@ -166,61 +168,61 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     constexpr int kVPieces = 2 * kStrips, kVRows = 64 / kVPieces;
     const int vpiece = lane % kVPieces, vrow0 = lane / kVPieces;
 
-  // scores of the chunk staged in S, into A: C(ms, mt)[s][t] = q_t . k_s
-  // (A = K rows s, B = Q rows t; lane holds column t = 16mt + r16, rows
-  // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s);
-  // two vertically stacked tiles are the chain-order A fragment (mt, kb)
-  // The fragments of the row blocks mt in the bit mask are formed (the
-  // caller passes Mask<bits>).
-  auto scores = [&](const Stage &S, u32x4 *A, auto mask_tag) {
-    constexpr int mask = decltype(mask_tag)::value;
-    constexpr int top = (mask & 8) ? 3 : (mask & 4) ? 2 : (mask & 2) ? 1 : 0;
-    auto frag = [&](const u32x4 *T, int mt, int kb) {
-      return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
-    };
-    bf16x8 qf[16];
+    // scores of the chunk staged in S, into A: C(ms, mt)[s][t] = q_t . k_s
+    // (A = K rows s, B = Q rows t; lane holds column t = 16mt + r16, rows
+    // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s);
+    // two vertically stacked tiles are the chain-order A fragment (mt, kb).
+    // Only the fragments of the row blocks mt in the bit mask are formed (the
+    // caller passes Mask<bits>).
+    auto scores = [&](const Stage &S, u32x4 *A, auto mask_tag) {
+      constexpr int mask = decltype(mask_tag)::value;
+      constexpr int top = (mask & 8) ? 3 : (mask & 4) ? 2 : (mask & 2) ? 1 : 0;
+      auto frag = [&](const u32x4 *T, int mt, int kb) {
+        return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
+      };
+      bf16x8 qf[16];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        if (mask & (1 << mt)) qf[4 * mt + kk] = frag(S.qr, mt, kk);
-    f32x4 sc[4][4]; // sc[mt][ms], ms <= mt
+        for (int kk = 0; kk < 4; ++kk)
+          if (mask & (1 << mt)) qf[4 * mt + kk] = frag(S.qr, mt, kk);
+      f32x4 sc[4][4]; // sc[mt][ms], ms <= mt
 #pragma unroll
-    for (int ms = 0; ms <= top; ++ms) {
-      bf16x8 kf[4];
+      for (int ms = 0; ms <= top; ++ms) {
+        bf16x8 kf[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[kk] = frag(S.kr, ms, kk);
+        for (int kk = 0; kk < 4; ++kk) kf[kk] = frag(S.kr, ms, kk);
 #pragma unroll
-      for (int mt = ms; mt < 4; ++mt) {
-        if (!(mask & (1 << mt))) continue;
-        f32x4 acc = zero4();
+        for (int mt = ms; mt < 4; ++mt) {
+          if (!(mask & (1 << mt))) continue;
+          f32x4 acc = zero4();
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[kk], qf[4 * mt + kk], acc);
-        sc[mt][ms] = acc;
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (!(mask & (1 << mt))) continue;
-      const int t = 16 * mt + r16;
-      const float g2t = S.g2[t];
-#pragma unroll
-      for (int ms = 0; ms <= mt; ++ms) {
-        const f32x4 g2s = *reinterpret_cast<const f32x4 *>(S.g2 + 16 * ms + 4 * q4);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int si = 16 * ms + 4 * q4 + ii;
-          sc[mt][ms][ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - g2s[ii]) * sc[mt][ms][ii] : 0.f;
+          for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[kk], qf[4 * mt + kk], acc);
+          sc[mt][ms] = acc;
         }
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (2 * kb > mt) continue;
-        const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
-        A[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
+      for (int mt = 0; mt < 4; ++mt) {
+        if (!(mask & (1 << mt))) continue;
+        const int t = 16 * mt + r16;
+        const float g2t = S.g2[t];
+#pragma unroll
+        for (int ms = 0; ms <= mt; ++ms) {
+          const f32x4 g2s = *reinterpret_cast<const f32x4 *>(S.g2 + 16 * ms + 4 * q4);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int si = 16 * ms + 4 * q4 + ii;
+            sc[mt][ms][ii] = (si <= t) ? __builtin_amdgcn_exp2f(g2t - g2s[ii]) * sc[mt][ms][ii] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (2 * kb > mt) continue;
+          const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
+          A[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
+        }
       }
-    }
-  };
+    };
     if (role == 0) {
       // ---- Q, K rows; outputs --------------------------------------------
       u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
