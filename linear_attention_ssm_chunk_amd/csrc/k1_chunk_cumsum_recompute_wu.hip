@@ -9,7 +9,7 @@
 //   L[r,s] = beta_r exp(G_r - G_s) (k_r . k_s)        (s < r, else 0)
 //   T'     = (I + L)^-1 diag(beta)                     (the UT transform)
 // so that U = T' V and W = T' diag(exp(G)) K.  This stage emits T' itself
-// (12 KB per chunk-head) instead of W and U (64 KB in float32): the spine forms
+// (10 KB per chunk-head) instead of W and U (64 KB in float32): the spine forms
 // uc = U - W h = T' (V - diag(exp(G)) K h) on the fly from T', K and V.
 //
 // One wave per (chunk, v-head):
@@ -21,9 +21,10 @@
 //     substitution, one lane per column (32 rows, <= 496 FMAs per lane);
 //   * the off-diagonal block T21 = -T22 (L21 T11) on MFMA, every operand split
 //     into bf16 hi + lo (three products each, ~2^-17 relative error);
-//   * T' = T diag(beta), split hi/lo, stored in the exact A-operand fragment
-//     order the spine reads (hi and lo: the 6 nonzero fragments x 64 lanes x
-//     16 bytes each).
+//   * T' = T diag(beta), split hi/lo, stored in the A-operand fragment order
+//     the spine reads (hi and lo: the 6 nonzero fragments x 64 lanes x 16
+//     bytes, of which the two diagonal fragments keep only the first 8 bytes
+//     per lane, their other half being the zero block above the diagonal).
 #include "gdn_device.h"
 
 namespace gdn {
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
   // holds rows t = 16mt + r16, columns s = 32kb + {4q..4q+3, 16+4q..16+4q+3};
   // only the six with mt >= 2kb are stored (T' is lower triangular): the hi
   // parts, then the lo parts, 16 bytes per lane ------------------------------
-  u32x4 *dst = reinterpret_cast<u32x4 *>(p.tp + slot * (kTpBytes / 2));
+  char *dst = reinterpret_cast<char *>(p.tp + slot * (kTpBytes / 2));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -200,8 +201,15 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
                           b[0] * Bs[s1], b[1] * Bs[s1 + 1], b[2] * Bs[s1 + 2], b[3] * Bs[s1 + 3]};
       bf16x8 hi, lo;
       split8(x, hi, lo);
-      dst[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
-      dst[(kTpFrags + tri_frag(mt, kb)) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
+      const int f = tri_frag(mt, kb);
+      const u32x4 h4 = __builtin_bit_cast(u32x4, hi), l4 = __builtin_bit_cast(u32x4, lo);
+      if (tp_half(f)) { // columns 32kb + 16.. are above the diagonal: zero
+        *reinterpret_cast<u32x2 *>(dst + tp_offset(f) + 8 * lane) = u32x2{h4[0], h4[1]};
+        *reinterpret_cast<u32x2 *>(dst + kTpPartBytes + tp_offset(f) + 8 * lane) = u32x2{l4[0], l4[1]};
+      } else {
+        *reinterpret_cast<u32x4 *>(dst + tp_offset(f) + 16 * lane) = h4;
+        *reinterpret_cast<u32x4 *>(dst + kTpPartBytes + tp_offset(f) + 16 * lane) = l4;
+      }
     }
 }
 

@@ -292,9 +292,18 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     u32x4 vx[kVPieces];
     auto fetch = [&](int c) {
       const int64_t sl = slot_of(p, s, h, c);
-      const u32x4 *tsrc = reinterpret_cast<const u32x4 *>(p.tp + sl * (kTpBytes / 2));
+      const char *tsrc = reinterpret_cast<const char *>(p.tp + sl * (kTpBytes / 2));
 #pragma unroll
-      for (int f = 0; f < 2 * kTpFrags; ++f) tx[f] = tsrc[f * 64 + lane];
+      for (int f = 0; f < 2 * kTpFrags; ++f) {
+        const int fr = f % kTpFrags;
+        const char *fp = tsrc + (f / kTpFrags) * kTpPartBytes + tp_offset(fr);
+        if (tp_half(fr)) { // the zero half above the diagonal is not stored
+          const u32x2 x = *reinterpret_cast<const u32x2 *>(fp + 8 * lane);
+          tx[f] = u32x4{x[0], x[1], 0u, 0u};
+        } else {
+          tx[f] = *reinterpret_cast<const u32x4 *>(fp + 16 * lane);
+        }
+      }
       d0 = p.dec[sl * 2 * kChunk + lane];
       d1 = p.dec[sl * 2 * kChunk + kChunk + lane];
       gg = p.gc[sl * kChunk + lane];

@@ -11,6 +11,8 @@ import torch
 from . import binding as B
 from .inputs import CHUNK, HEAD_DIM, pack_contiguous, pack_conv
 
+TP_PART = 2560  # bf16 elements of one part (hi or lo) of a slot's T' (include/gdn_prefill.h)
+
 
 def _to_bf16_tensor(u16, device):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(device).view(torch.bfloat16)
@@ -162,7 +164,7 @@ class DeviceProblem:
         if name == "dec":
             return self.scratch[off:off + S * 2 * CHUNK * 4].view(torch.float32).view(S, 2, CHUNK)
         if name == "tp":
-            return self.scratch[off:off + S * 2 * 6 * 64 * 8 * 2].view(torch.bfloat16).view(S, 2, 6, 64, 8)
+            return self.scratch[off:off + S * 2 * TP_PART * 2].view(torch.bfloat16).view(S, 2, TP_PART)
         if name == "s_entry":
             return self.scratch[off:off + S * HEAD_DIM * HEAD_DIM * 2].view(torch.bfloat16).view(S, HEAD_DIM, HEAD_DIM)
         raise KeyError(name)

@@ -32,32 +32,42 @@ def relfro(a, b):
     return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
 
 
+# element offset of fragment f in a part, and whether it keeps only the first
+# 4 bf16 per lane (the diagonal fragments f = 0, 4, whose other half lies above
+# the diagonal)
+_TP_OFF = (0, 256, 768, 1280, 1792, 2048)
+_TP_HALF = (True, False, False, False, True, False)
+
+
 def _tp_index():
-    """Row / column of each element of the stored T' fragments: fragment f of the
-    six lower-triangular (mt, kb) (f = mt for kb = 0, f = mt + 2 for kb = 1),
-    lane 16q + r holds row 16mt + r, columns 32kb + 4q + e and 32kb + 16 + 4q + e."""
-    t = np.zeros((6, 64, 8), dtype=np.int64)
-    sc = np.zeros((6, 64, 8), dtype=np.int64)
+    """Row / column of each stored element of one T' part (2560 bf16): fragment
+    f of the six lower-triangular (mt, kb) (f = mt for kb = 0, f = mt + 2 for
+    kb = 1), lane 16q + r holds row 16mt + r, columns 32kb + 4q + e and
+    32kb + 16 + 4q + e; the diagonal fragments hold only the first four."""
+    t = np.zeros(2560, dtype=np.int64)
+    sc = np.zeros(2560, dtype=np.int64)
     for mt in range(4):
         for kb in range(2):
             if 2 * kb > mt:
                 continue
             f = mt if kb == 0 else mt + 2
+            per = 4 if _TP_HALF[f] else 8
             for lane in range(64):
                 q, r = lane // 16, lane % 16
-                for e in range(8):
-                    t[f, lane, e] = 16 * mt + r
-                    sc[f, lane, e] = 32 * kb + (4 * q + e if e < 4 else 16 + 4 * q + e - 4)
+                for e in range(per):
+                    i = _TP_OFF[f] + lane * per + e
+                    t[i] = 16 * mt + r
+                    sc[i] = 32 * kb + (4 * q + e if e < 4 else 16 + 4 * q + e - 4)
     return t, sc
 
 
 _TP_T, _TP_S = _tp_index()
 
 
-def unpack_tp(frags):
-    """T' [64, 64] from the documented fragment layout [2][6][64][8] (part 0 hi,
-    part 1 lo); the fragments above the diagonal blocks are not stored (0)."""
-    f = np.asarray(frags, dtype=np.float64)
+def unpack_tp(parts):
+    """T' [64, 64] from the documented layout [2][2560] (part 0 hi, part 1 lo);
+    elements not stored are 0."""
+    f = np.asarray(parts, dtype=np.float64)
     T = np.zeros((64, 64))
     T[_TP_T, _TP_S] = f[0] + f[1]
     return T
