@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 WARMUP_MIN_S = 0.05            # untimed warm-up floor: clocks reach steady state (see docstring)
 KERNELS = {1: "chunk_cumsum_recompute_wu", 2: "chunk_delta_h_fwd_o"}
-KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h_fwd_o.hip"}
+KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h_fwd_o.hip", 3: "k3_recurrent_decode.hip"}
 
 
 # ---------------------------------------------------------------------------
@@ -81,10 +81,11 @@ def algorithmic(p):
 
 
 def source_sha(stage):
-    path = os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", KERNEL_SRC[stage])
+    """Hash of what a kernel is built from: its source and the two headers."""
+    csrc = os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc")
     h = hashlib.sha256()
-    for f in (path, os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", "gdn_device.h")):
-        with open(f, "rb") as fh:
+    for f in (KERNEL_SRC[stage], "gdn_device.h", "gdn_params.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -266,12 +267,7 @@ def traffic_for_decode():
         return None
     with open(path) as f:
         t = json.load(f)
-    src = os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", "k3_recurrent_decode.hip")
-    h = hashlib.sha256()
-    for f in (src, os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc", "gdn_device.h")):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    if t.get("source_sha256") != h.hexdigest():
+    if t.get("source_sha256") != source_sha(3):
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -174,6 +174,10 @@ int gdn_prefill_validate(const void *q, const void *k, const void *v, const floa
  *               NULL.
  *   stream      hipStream_t.
  * A ragged sequence of length 0 leaves its state unchanged and writes nothing.
+ * Size limits (GDN_EINVAL beyond them): 1 <= B <= 65535; chunk slots per head
+ * (B * ceil(T/64), or total_chunks) <= INT32_MAX; ceil8(chunks of the longest
+ * sequence) * nv * 64 < 2^32 and ceil8(B * nk) * (nv/nk) * 1024 < 2^32 (the
+ * two launches count work-items in 32 bits).
  */
 int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
                 void *h_state, int h_state_is_table, void *out, void *scratch,
@@ -218,7 +222,7 @@ int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *
  *   h_state  as for gdn_prefill (contiguous [B][nv][dk][dv], or a device
  *            table of B pointers to [nv][dk][dv]), updated in place.
  *   out      bf16 [B][nv][dv], contiguous.
- * dk = dv = 128.  No scratch; one launch on `stream`, no synchronisation.
+ * dk = dv = 128; 1 <= B <= 65535; nv * 256 < 2^32 (work-items of the launch).  No scratch; one launch on `stream`, no synchronisation.
  * Returns GDN_OK or an error as gdn_prefill does; gdn_decode_validate runs the
  * same checks without touching the GPU.
  */

@@ -7,6 +7,7 @@
 // path that cannot run fails loudly; nothing here falls back to anything.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -40,6 +41,29 @@ int ok() {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned(const void *ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// A dispatch counts its work-items in 32 bits per grid dimension.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+
+// Grid extents of the two prefill launches (the launchers' own formulas), and
+// the int fields of the parameter block, checked before anything is launched.
+int check_extents(int B, int T, int nk, int nv, const gdn_varlen *varlen) {
+  const int64_t per_seq = varlen ? varlen->max_chunks : (int64_t(T) + GDN_CHUNK - 1) / GDN_CHUNK;
+  const int64_t total = varlen ? varlen->total_chunks : int64_t(B) * per_seq;
+  if (total > INT32_MAX)
+    return fail(GDN_EINVAL, "sizes: B=%d x %lld chunks per sequence exceeds %d chunk slots per head", B,
+                (long long)per_seq, INT32_MAX);
+  // stage 1: one 64-lane workgroup per (chunk rounded up to 8, v-head)
+  if (((per_seq + 7) / 8) * 8 * nv * 64 > kMaxWorkItems)
+    return fail(GDN_EINVAL, "sizes: %lld chunks per sequence x nv=%d exceed the stage-1 grid", (long long)per_seq,
+                nv);
+  // stage 2: at most two 512-lane workgroups per (sequence, v-head) chain, the
+  // k-groups rounded up to 8 (one or two strips per workgroup are only chosen
+  // when there are fewer chains than compute units)
+  if (((int64_t(B) * nk + 7) / 8) * 8 * (nv / nk) * 2 * 512 > kMaxWorkItems)
+    return fail(GDN_EINVAL, "sizes: B=%d x nv=%d chains exceed the stage-2 grid", B, nv);
+  return GDN_OK;
+}
 
 // Chunk slots per head, or -1 when the sizes are invalid.
 int64_t chunk_slots(int B, int T, const gdn_varlen *varlen) {
@@ -84,7 +108,6 @@ int validate(const void *q, const void *k, const void *v, const float *g, const 
     return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
   if (nk <= 0 || nv <= 0) return fail(GDN_EINVAL, "head counts: nk=%d nv=%d must be positive", nk, nv);
   if (nv % nk != 0) return fail(GDN_EINVAL, "GQA grouping: nv=%d is not a multiple of nk=%d", nv, nk);
-  if (nv > 65535) return fail(GDN_EINVAL, "nv=%d exceeds the grid's y extent (65535)", nv);
   if (B <= 0 || B > 65535) return fail(GDN_EINVAL, "B=%d must be in 1..65535", B);
   if (varlen == nullptr && T <= 0) return fail(GDN_EINVAL, "T=%d must be positive for dense input", T);
   if (varlen != nullptr && T < 0) return fail(GDN_EINVAL, "T=%d (total tokens) must be >= 0", T);
@@ -136,7 +159,9 @@ int validate(const void *q, const void *k, const void *v, const float *g, const 
     if (int64_t(varlen->total_chunks) * GDN_CHUNK < int64_t(T))
       return fail(GDN_EINVAL, "ragged: total_chunks=%d cannot hold T=%d tokens", varlen->total_chunks, T);
   }
-  int rc = layout(B, T, nk, nv, dk, dv, varlen, lay);
+  int rc = check_extents(B, T, nk, nv, varlen);
+  if (rc != GDN_OK) return rc;
+  rc = layout(B, T, nk, nv, dk, dv, varlen, lay);
   if (rc != GDN_OK) return rc;
   if (scratch_bytes < lay->total)
     return fail(GDN_ESCRATCH, "scratch: %zu bytes given, %zu needed", scratch_bytes, lay->total);
@@ -200,7 +225,9 @@ int validate_decode(const void *q, const void *k, const void *v, const float *g,
     return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
   if (nk <= 0 || nv <= 0) return fail(GDN_EINVAL, "head counts: nk=%d nv=%d must be positive", nk, nv);
   if (nv % nk != 0) return fail(GDN_EINVAL, "GQA grouping: nv=%d is not a multiple of nk=%d", nv, nk);
-  if (nv > (1 << 24)) return fail(GDN_EINVAL, "nv=%d is too large for the grid", nv);
+  // one 64-lane workgroup per 32 columns of each v-head
+  if (int64_t(nv) * (GDN_HEAD_DIM / 32) * 64 > kMaxWorkItems)
+    return fail(GDN_EINVAL, "nv=%d is too large for the decode grid", nv);
   if (B <= 0 || B > 65535) return fail(GDN_EINVAL, "B=%d must be in 1..65535", B);
   if (!q || !k || !v) return fail(GDN_EINVAL, "null pointer: q, k and v are required");
   if (!g || !beta) return fail(GDN_EINVAL, "null pointer: g and beta are required");

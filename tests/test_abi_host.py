@@ -93,6 +93,22 @@ def test_each_guard_rejects_by_name(over, code, needle):
     assert needle in msg
 
 
+def test_grid_extent_guards():
+    """Sizes whose launches would overflow a 32-bit work-item count, or the
+    int chunk count of the parameter block, are rejected before any launch."""
+    # B x ceil(T/64) chunk slots beyond INT32_MAX
+    rc, msg = validate(B=65535, T=2 ** 31 - 1)
+    assert rc == B.GDN_EINVAL and "chunk slots" in msg, msg
+    # one long sequence: 2^25 chunks x 4 heads x 64 lanes = 2^33 work-items in stage 1
+    rc, msg = validate(B=1, T=2 ** 31 - 1)
+    assert rc == B.GDN_EINVAL and "stage-1 grid" in msg, msg
+    # stage 2 launches up to 2 workgroups x 512 lanes per chain: 65535 x 65
+    # chains exceed 2^32 work-items, 65535 x 64 (2^32 - 2^16 x 1024) do not
+    rc, msg = validate(B=65535, T=64, nk=65, nv=65, strides=(65 * 128, 65 * 128, 65))
+    assert rc == B.GDN_EINVAL and "stage-2 grid" in msg, msg
+    assert validate(B=65535, T=64, nk=64, nv=64, strides=(64 * 128, 64 * 128, 64))[0] == B.GDN_OK
+
+
 def test_ragged_guards():
     vl = B.gdn_varlen(P + 64, P + 128, 3, 5)
     rc, msg = validate(varlen=vl, T=300, scratch_bytes=B.gdn_prefill_scratch_bytes(2, 300, 2, 4, 128, 128, vl))
@@ -187,6 +203,11 @@ def test_decode_validation_names_the_guard():
     assert rc == B.GDN_EINVAL and "gb_row" in msg
     # a table of state pointers only needs 8-byte alignment
     assert decode_validate(h_state=P + 8, h_state_is_table=1)[0] == B.GDN_OK
+    # 2^24 heads x 4 workgroups x 64 lanes = 2^32 work-items; one head fewer fits
+    rc, msg = decode_validate(nk=1, nv=2 ** 24, strides=B.gdn_strides(128, 2 ** 31, 2 ** 24))
+    assert rc == B.GDN_EINVAL and "decode grid" in msg, msg
+    nv = 2 ** 24 - 1
+    assert decode_validate(nk=1, nv=nv, strides=B.gdn_strides(128, nv * 128, nv))[0] == B.GDN_OK
 
 
 def test_decode_rejects_without_touching_the_gpu():
