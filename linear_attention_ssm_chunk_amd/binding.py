@@ -2,8 +2,8 @@
 
 Argument marshalling only: every function here converts its arguments to C
 types and calls the function of the same name in the library.  Pointer
-arguments take an int (a device address) or any object with ``data_ptr()``
-(a torch tensor).  The library must have been built
+arguments take an int (a device address) or a tensor in device memory (an
+object with ``data_ptr()``; one in host memory raises ValueError).  The library must have been built
 (``python -m linear_attention_ssm_chunk_amd.build``); if it is missing, loading
 fails with an error -- there is no other code path.
 """
@@ -83,9 +83,13 @@ def lib():
 
 
 def _ptr(x):
+    """Device address of x.  A tensor in host memory is refused here: the
+    kernels would dereference its address on the GPU."""
     if x is None:
         return None
     if hasattr(x, "data_ptr"):
+        if getattr(x, "is_cuda", True) is not True:
+            raise ValueError(f"tensor on {x.device}: every pointer argument must be in device memory")
         return x.data_ptr()
     return int(x)
 
@@ -165,6 +169,8 @@ def gdn_prefill_scratch_layout(B, T, nk, nv, dk, dv, varlen=None):
 
 def gdn_varlen_check_host(B, cu_seqlens, cu_chunks, max_chunks, total_chunks):
     """Check host copies of the ragged offsets (sequences of ints)."""
+    if len(cu_seqlens) < B + 1 or len(cu_chunks) < B + 1:
+        raise ValueError(f"offsets: {len(cu_seqlens)} and {len(cu_chunks)} entries given, B + 1 = {B + 1} needed")
     a = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
     b = (ctypes.c_int32 * len(cu_chunks))(*[int(x) for x in cu_chunks])
     return lib().gdn_varlen_check_host(B, a, b, int(max_chunks), int(total_chunks))

@@ -73,8 +73,11 @@ class DeviceProblem:
             self._cu_s = torch.from_numpy(self.cu_seqlens_host).to(device)
             self._cu_c = torch.from_numpy(self.cu_chunks_host).to(device)
             nch = np.diff(self.cu_chunks_host)
-            self.varlen = B.gdn_varlen(self._cu_s.data_ptr(), self._cu_c.data_ptr(),
-                                       int(nch.max()) if len(nch) else 0, int(self.cu_chunks_host[-1]))
+            max_c, total_c = (int(nch.max()) if len(nch) else 0), int(self.cu_chunks_host[-1])
+            # the library trusts device offsets; check the host copies once here
+            if B.gdn_varlen_check_host(self.nseq, self.cu_seqlens_host, self.cu_chunks_host, max_c, total_c) != B.GDN_OK:
+                raise ValueError(B.gdn_last_error())
+            self.varlen = B.gdn_varlen(self._cu_s.data_ptr(), self._cu_c.data_ptr(), max_c, total_c)
             self.B, self.T = self.nseq, self.N
         else:
             self.varlen = None

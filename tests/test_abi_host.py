@@ -162,6 +162,15 @@ def test_varlen_host_check():
     assert "decreases" in B.gdn_last_error()
     assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 2, 5) == B.GDN_EINVAL
     assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 3, 6) == B.GDN_EINVAL
+    # fewer than B + 1 offsets: refused before the library reads past them
+    with pytest.raises(ValueError):
+        B.gdn_varlen_check_host(4, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5)
+
+
+def test_host_tensors_are_refused():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="device memory"):
+        validate(q=torch.zeros(8, dtype=torch.bfloat16))
 
 
 def decode_args(**over):
