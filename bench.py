@@ -81,12 +81,15 @@ def algorithmic(p):
 
 
 def source_sha(stage):
-    """Hash of what a kernel is built from: its source and the two headers."""
+    """Hash of what a kernel is built from: its source, the device headers and
+    the build flags."""
+    from linear_attention_ssm_chunk_amd import build
     csrc = os.path.join(ROOT, "linear_attention_ssm_chunk_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SRC[stage], "gdn_device.h", "gdn_params.h"):
+    for f in [KERNEL_SRC[stage]] + sorted(f for f in os.listdir(csrc) if f.endswith(".h")):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(build.FLAGS[:-2]).encode())  # without the include path
     return h.hexdigest()
 
 

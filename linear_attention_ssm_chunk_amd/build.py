@@ -4,7 +4,9 @@
 
 Every HIP source is compiled with packed FP32 math disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns
-that it does not know the feature, which is harmless.
+that it does not know the feature, which is harmless.  MFMA results are kept
+in ordinary vector registers (``-amdgpu-mfma-vgpr-form``), which spares the
+UT solve a register move per accumulator element it reads back.
 """
 
 import os
@@ -20,7 +22,7 @@ SOURCES = ["gdn_api.hip", "k1_chunk_cumsum_recompute_wu.hip", "k2_chunk_delta_h_
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
