@@ -52,7 +52,7 @@ def algorithmic(p):
 
     Bytes: every operand each kernel must read or write once (q, k counted once
     per k-head).  Stage 1 reads k, g, beta and writes gc, the decays and T'
-    (10 KB per chunk-head); stage 2 reads q, k, v, gc, the decays, T' and the
+    (5 KB per chunk-head); stage 2 reads q, k, v, gc, the decays, T' and the
     state, and writes the entry states (32 KB per chunk-head), o and the state.
     Flops: the dense-tile MFMA work per chunk-head of what each kernel computes
     (Gram in stage 1; K h, T' R, K^T uc, Q h, the scores Q K^T and A uc in
@@ -67,7 +67,7 @@ def algorithmic(p):
     gb_bytes = N * nv * 8
     gc_bytes = slots * C * 4
     dec_bytes = slots * 2 * C * 4
-    tp_bytes = slots * 2 * 2560 * 2  # hi and lo parts of 2560 bf16 each
+    tp_bytes = slots * 2560 * 2  # 2560 float16
     s_bytes = slots * d * d * 2
     state_bytes = nseq * nv * d * d * 4
     o_bytes = N * nv * d * 2

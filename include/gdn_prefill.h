@@ -107,25 +107,24 @@ typedef struct gdn_varlen {
  *   gc      float [slots][64]        chunk-local cumulative log-gate G_t; rows
  *                                    past the sequence end repeat the last value
  *   dec     float [slots][2][64]     exp(G_t), then exp(G_{n-1} - G_t)
- *   tp      bf16  [slots][2][2560]   the UT transform T' = (I+L)^-1 diag(beta)
- *                                    (so U = T' V, W = T' diag(exp(G)) K) as
- *                                    bf16 hi (index 0) and lo (index 1) parts
- *                                    in MFMA fragment order.  Of the 16x32
- *                                    fragments (mt, kb) (rows 16mt.., columns
- *                                    32kb..) only the lower-triangular six,
- *                                    mt >= 2kb, are stored, in the order
+ *   tp      f16   [slots][2560]      the UT transform T' = (I+L)^-1 diag(beta)
+ *                                    (so U = T' V, W = T' diag(exp(G)) K) in
+ *                                    float16, in MFMA fragment order.  Of the
+ *                                    16x32 fragments (mt, kb) (rows 16mt..,
+ *                                    columns 32kb..) only the lower-triangular
+ *                                    six, mt >= 2kb, are stored, in the order
  *                                    f = mt for kb = 0 and f = mt + 2 for
  *                                    kb = 1; lane l = 16q + r of fragment f
  *                                    holds row t = 16mt + r, columns
  *                                    s = 32kb + 4q + e (e = 0..3) and
- *                                    s = 32kb + 16 + 4q + e, as 8 bf16 per lane
- *                                    (512 elements per fragment), except the
- *                                    diagonal fragments f = 0 and f = 4
+ *                                    s = 32kb + 16 + 4q + e, as 8 values per
+ *                                    lane (512 elements per fragment), except
+ *                                    the diagonal fragments f = 0 and f = 4
  *                                    (mt = 2kb), which hold only the first 4
  *                                    per lane (256 elements): their other
  *                                    columns lie above the diagonal.  Element
- *                                    offsets of f = 0..5 in a part: 0, 256,
- *                                    768, 1280, 1792, 2048
+ *                                    offsets of f = 0..5: 0, 256, 768, 1280,
+ *                                    1792, 2048
  *   s_entry bf16  [slots][128][128]  entry state of each chunk as S = h^T
  *                                    ([dv][dk], the recurrence's orientation);
  *                                    dense input: [B][nv][T/64][dv][dk]

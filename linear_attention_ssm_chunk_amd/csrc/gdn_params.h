@@ -15,13 +15,12 @@ constexpr int kDim = 128;     // dk = dv
 constexpr int kTpFrags = 6;                              // nonzero 16x32 fragments of T' (lower triangle)
 constexpr int64_t kGcBytes = int64_t(kChunk) * 4;        // G_t
 constexpr int64_t kDecBytes = int64_t(2) * kChunk * 4;   // exp(G_t), exp(G_{n-1} - G_t)
-// T' per slot: hi part, then lo part, each the six fragments in order f; the
-// two diagonal fragments (f = 0, 4) keep only their first 8 bytes per lane
-// (their other half is the zero block above the diagonal).
-constexpr int kTpPartBytes = (4 * 16 + 2 * 8) * 64;        // 5 KB
-constexpr int64_t kTpBytes = int64_t(2) * kTpPartBytes;       // 10 KB
+// T' per slot: float16, the six fragments in order f, 8 values (16 bytes) per
+// lane; the two diagonal fragments (f = 0, 4) keep only their first 4 (8
+// bytes): their other half is the zero block above the diagonal.
+constexpr int64_t kTpBytes = (4 * 16 + 2 * 8) * 64;        // 5 KB
 constexpr bool tp_half(int f) { return f == 0 || f == 4; }
-constexpr int tp_offset(int f) {          // byte offset of fragment f in a part
+constexpr int tp_offset(int f) {          // byte offset of fragment f
   return f == 0 ? 0 : f == 1 ? 512 : f == 2 ? 1536 : f == 3 ? 2560 : f == 4 ? 3584 : 4096;
 }
 constexpr int64_t kSBytes = int64_t(kDim) * kDim * 2;    // entry state, bf16 [dv][dk]

@@ -21,9 +21,10 @@
 //   * the off-diagonal tiles of the two diagonal 32x32 blocks, then the lower
 //     left 32x32 block, by the formula above on MFMA, every operand split
 //     into bf16 hi + lo (three products each, ~2^-17 relative error);
-//   * T' = T diag(beta), split hi/lo, in the A-operand fragment order of the
-//     spine: fragment f = tri_frag(mt, kb) (mt >= 2kb) holds, in lane
-//     16q + r, row t = 16mt + r, columns s = 32kb + 4q + e and
+//   * T' = T diag(beta), rounded to float16 (11 significant bits: the spine
+//     splits each value exactly into bf16 hi + lo), in the A-operand fragment
+//     order of the spine: fragment f = tri_frag(mt, kb) (mt >= 2kb) holds, in
+//     lane 16q + r, row t = 16mt + r, columns s = 32kb + 4q + e and
 //     32kb + 16 + 4q + e (e = 0..3).  In the diagonal fragments (mt = 2kb)
 //     the second four lie above the diagonal and are 0.
 #pragma once
@@ -103,12 +104,18 @@ __device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[4][4], const uint16_t 
   }
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Two floats -> two float16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
 // Gate scan and UT solve of one chunk by one wave.  In: kf (above), gv / bv
 // the g and beta of token `lane` (0 for lanes >= n).  Out: G = G_lane (lanes
-// past the end repeat G_{n-1}), Gn = G_{n-1}, and T' as tx[f] (hi parts,
-// f = 0..5) and tx[6 + f] (lo parts).  W is private to the wave for the call.
+// past the end repeat G_{n-1}), Gn = G_{n-1}, and T' as tx[f] (8 float16 per
+// lane, f = 0..5).  W is private to the wave for the call.
 __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, float bv, int n, UtWork &W,
-                                         int lane, u32x4 (&tx)[2 * kTpFrags], float &G, float &Gn) {
+                                         int lane, u32x4 (&tx)[kTpFrags], float &G, float &Gn) {
   const int q4 = lane >> 4, r16 = lane & 15;
   const SplitK sp;
   auto tile = [&](int mr, int ms) -> float * { return W.L + tri_tile(mr, ms) * kTileF; };
@@ -264,30 +271,23 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
     }
   }
 
-  // ---- T' = T diag(beta), hi / lo, in fragment order -----------------------
+  // ---- T' = T diag(beta), float16, in fragment order ----------------------
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (2 * kb > mt) continue;
       const int s0 = 32 * kb + 4 * q4;
-      const int f = tri_frag(mt, kb);
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(tile(mt, 2 * kb) + r16 * kTP + 4 * q4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(W.Bs + s0);
-      if (2 * kb == mt) { // the second four columns lie above the diagonal
-        bf16x4 hi, lo;
-        sp.four(a * b0, hi, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi), l2 = __builtin_bit_cast(u32x2, lo);
-        tx[f] = u32x4{h2[0], h2[1], 0u, 0u};
-        tx[kTpFrags + f] = u32x4{l2[0], l2[1], 0u, 0u};
-      } else {
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(tile(mt, 2 * kb + 1) + r16 * kTP + 4 * q4);
-        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(W.Bs + s0 + 16);
-        bf16x8 hi, lo;
-        sp.eight(a * b0, b * b1, hi, lo);
-        tx[f] = __builtin_bit_cast(u32x4, hi);
-        tx[kTpFrags + f] = __builtin_bit_cast(u32x4, lo);
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(tile(mt, 2 * kb) + r16 * kTP + 4 * q4) *
+                      *reinterpret_cast<const f32x4 *>(W.Bs + s0);
+      u32x4 out = {cvt_pk_f16(a[0], a[1]), cvt_pk_f16(a[2], a[3]), 0u, 0u};
+      if (2 * kb + 1 <= mt) { // else the second four columns lie above the diagonal
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(tile(mt, 2 * kb + 1) + r16 * kTP + 4 * q4) *
+                        *reinterpret_cast<const f32x4 *>(W.Bs + s0 + 16);
+        out[2] = cvt_pk_f16(b[0], b[1]);
+        out[3] = cvt_pk_f16(b[2], b[3]);
       }
+      tx[tri_frag(mt, kb)] = out;
     }
 }
 

@@ -3,14 +3,14 @@
 // Page "spark_model/layers/ops/ssm_gdn_a3.rs", doc comment of gdn_prefill_fla,
 // stage 1: per chunk and v-head, the chunk-local cumulative log-gate gc and the
 // WY/UT solve (gdn_ut_solve.h), written to the scratch: gc, the decays
-// exp(G_t) and exp(G_{n-1} - G_t), and T' = (I+L)^-1 diag(beta) (10 KB per
+// exp(G_t) and exp(G_{n-1} - G_t), and T' = (I+L)^-1 diag(beta) (5 KB per
 // chunk-head, so that U = T' V and W = T' diag(exp(G)) K) -- not W and U
 // (64 KB in float32).
 //
-// One wave per (chunk, v-head).  T' leaves as bf16 hi and lo parts in the
-// spine's A-operand fragment order: the 6 nonzero fragments x 64 lanes x 16
-// bytes, of which the two diagonal fragments keep only the first 8 bytes per
-// lane (their other half is the zero block above the diagonal).
+// One wave per (chunk, v-head).  T' leaves in float16 in the spine's A-operand
+// fragment order: the 6 nonzero fragments x 64 lanes x 16 bytes, of which the
+// two diagonal fragments keep only the first 8 bytes per lane (their other
+// half is the zero block above the diagonal).
 #include "gdn_ut_solve.h"
 
 namespace gdn {
@@ -40,24 +40,20 @@ __global__ __launch_bounds__(64) void chunk_cumsum_recompute_wu(Params p) {
     gv = p.g[off];
     bv = p.beta[off];
   }
-  u32x4 tx[2 * kTpFrags];
+  u32x4 tx[kTpFrags];
   float G, Gn;
   ut_solve(kf, gv, bv, n, work, lane, tx, G, Gn);
 
   p.gc[slot * kChunk + lane] = G;
   p.dec[slot * 2 * kChunk + lane] = expf(G);
   p.dec[slot * 2 * kChunk + kChunk + lane] = expf(Gn - G);
-  char *dst = reinterpret_cast<char *>(p.tp + slot * (kTpBytes / 2));
+  char *dst = reinterpret_cast<char *>(p.tp) + slot * kTpBytes;
 #pragma unroll
   for (int f = 0; f < kTpFrags; ++f) {
-    if (tp_half(f)) { // the second half lies above the diagonal: zero, not stored
+    if (tp_half(f)) // the second half lies above the diagonal: zero, not stored
       *reinterpret_cast<u32x2 *>(dst + tp_offset(f) + 8 * lane) = u32x2{tx[f][0], tx[f][1]};
-      *reinterpret_cast<u32x2 *>(dst + kTpPartBytes + tp_offset(f) + 8 * lane) =
-          u32x2{tx[kTpFrags + f][0], tx[kTpFrags + f][1]};
-    } else {
+    else
       *reinterpret_cast<u32x4 *>(dst + tp_offset(f) + 16 * lane) = tx[f];
-      *reinterpret_cast<u32x4 *>(dst + kTpPartBytes + tp_offset(f) + 16 * lane) = tx[kTpFrags + f];
-    }
   }
 }
 

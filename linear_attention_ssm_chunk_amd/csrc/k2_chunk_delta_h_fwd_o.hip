@@ -28,11 +28,11 @@
 //     active pair stages chunk c+1 into the free half of a double-buffered
 //     LDS stage, from registers it filled two steps earlier, then fetches
 //     chunk c+3: role 0 the Q and K rows (1 KB per load), role 1 the T'
-//     fragments, decays, gate sums and V rows.  The idle pair works on chunk
-//     c, visible in the stage compute reads: role 1 reads the Q and K row
-//     fragments and forms the causal decayed scores A of chunk c on MFMA
-//     (for S = 4 role 0 forms half of them); role 0 stores the output tile of
-//     chunk c-2.
+//     fragments (float16), decays, gate sums and V rows.  The idle pair works
+//     on chunk c, visible in the stage compute reads: role 1 splits the T' it
+//     fetched last into bf16 hi + lo, reads the Q and K row fragments and
+//     forms the causal decayed scores A of chunk c on MFMA (for S = 4 role 0
+//     forms half of them); role 0 stores the output tile of chunk c-2.
 //     The compute waves read K^T and their V tiles out of the row tiles with
 //     transposing LDS reads.
 // One barrier per chunk (and one after the last).  Entry states leave as
@@ -44,15 +44,16 @@
 // step and read in the next, and written again only after the barrier that
 // ends the reading step.
 // Precision: h is float32 between chunks; h, R and the decayed uc are split
-// into bf16 hi+lo for the products that feed the state (K is exact in bf16, T'
-// arrives split), so every product keeps ~2^-17 relative error with bf16 MFMA
-// and float32 accumulation.  The output uses bf16(h) and bf16(uc) -- the
+// into bf16 hi+lo for the products that feed the state (K is exact in bf16;
+// T', stored in float16, splits exactly), so every product keeps ~2^-17
+// relative error with bf16 MFMA and float32 accumulation, on top of T''s own
+// float16 rounding (2^-11).  The output uses bf16(h) and bf16(uc) -- the
 // page's stage 3 reads both in bf16 -- with float32 accumulation.
 //
 // Workgroup order: all workgroups that read one k-head's rows (its r v-heads
 // x column groups) get the same blockIdx.x % 8, so that on a round-robin XCD
 // dispatch they share one XCD's L2.
-#include "gdn_device.h"
+#include "gdn_ut_solve.h" // SplitK
 
 namespace gdn {
 
@@ -287,21 +288,20 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     }
 
     // ---- T', decays, gate sums, V rows; scores ------------------------------
-    u32x4 tx[2 * kTpFrags];
+    u32x4 t16[kTpFrags];     // T' of the chunk fetched last, float16
+    u32x4 tx[2 * kTpFrags];  // T' of the chunk stashed next: bf16 hi (f), lo (6 + f)
     float d0 = 0.f, d1 = 0.f, gg = 0.f;
     u32x4 vx[kVPieces];
     auto fetch = [&](int c) {
       const int64_t sl = slot_of(p, s, h, c);
-      const char *tsrc = reinterpret_cast<const char *>(p.tp + sl * (kTpBytes / 2));
+      const char *tsrc = reinterpret_cast<const char *>(p.tp) + sl * kTpBytes;
 #pragma unroll
-      for (int f = 0; f < 2 * kTpFrags; ++f) {
-        const int fr = f % kTpFrags;
-        const char *fp = tsrc + (f / kTpFrags) * kTpPartBytes + tp_offset(fr);
-        if (tp_half(fr)) { // the zero half above the diagonal is not stored
-          const u32x2 x = *reinterpret_cast<const u32x2 *>(fp + 8 * lane);
-          tx[f] = u32x4{x[0], x[1], 0u, 0u};
+      for (int f = 0; f < kTpFrags; ++f) {
+        if (tp_half(f)) { // the zero half above the diagonal is not stored
+          const u32x2 x = *reinterpret_cast<const u32x2 *>(tsrc + tp_offset(f) + 8 * lane);
+          t16[f] = u32x4{x[0], x[1], 0u, 0u};
         } else {
-          tx[f] = *reinterpret_cast<const u32x4 *>(fp + 16 * lane);
+          t16[f] = *reinterpret_cast<const u32x4 *>(tsrc + tp_offset(f) + 16 * lane);
         }
       }
       d0 = p.dec[sl * 2 * kChunk + lane];
@@ -316,6 +316,24 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         vx[jj] = *reinterpret_cast<const u32x4 *>(vc + off);
       }
     };
+    // float16 T' -> bf16 hi + lo, exactly: 11 significant bits leave at most
+    // 3 for x - hi
+    auto decode = [&]() {
+      const SplitK sp;
+#pragma unroll
+      for (int f = 0; f < kTpFrags; ++f) {
+        uint32_t hw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int w = 0; w < (tp_half(f) ? 2 : 4); ++w) {
+          const uint32_t x = t16[f][w];
+          const float a = float(__builtin_bit_cast(_Float16, uint16_t(x & 0xFFFFu)));
+          const float b = float(__builtin_bit_cast(_Float16, uint16_t(x >> 16)));
+          sp.pair(a, b, hw[w], lw[w]);
+        }
+        tx[f] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        tx[kTpFrags + f] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+      }
+    };
     auto stash = [&](Stage &S) {
 #pragma unroll
       for (int f = 0; f < 2 * kTpFrags; ++f) S.tp[f * 64 + lane] = tx[f];
@@ -325,7 +343,10 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
       for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
-    if (pair < nch) fetch(pair);
+    if (pair < nch) {
+      fetch(pair);
+      decode();
+    }
     if (pair == 0) {
       stash(st[0]);
       if (2 < nch) fetch(2);
@@ -336,7 +357,9 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         stash(st[(c + 1) & 1]);
         if (c + 3 < nch) fetch(c + 3);
       }
-      // the idle pair forms the scores of chunk c (with role 0 for S = 4)
+      // the idle pair splits the T' it fetched last (chunk c+2, stashed in
+      // step c+1) and forms the scores of chunk c (with role 0 for S = 4)
+      if ((c & 1) == pair && c + 2 < nch) decode();
       if ((c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<kStrips == 4 ? 0x6 : 0xF>());
       __syncthreads();
     }

@@ -11,7 +11,7 @@ import torch
 from . import binding as B
 from .inputs import CHUNK, HEAD_DIM, pack_contiguous, pack_conv
 
-TP_PART = 2560  # bf16 elements of one part (hi or lo) of a slot's T' (include/gdn_prefill.h)
+TP_ELEMS = 2560  # float16 elements of a slot's T' (include/gdn_prefill.h)
 
 
 def _to_bf16_tensor(u16, device):
@@ -167,7 +167,7 @@ class DeviceProblem:
         if name == "dec":
             return self.scratch[off:off + S * 2 * CHUNK * 4].view(torch.float32).view(S, 2, CHUNK)
         if name == "tp":
-            return self.scratch[off:off + S * 2 * TP_PART * 2].view(torch.bfloat16).view(S, 2, TP_PART)
+            return self.scratch[off:off + S * TP_ELEMS * 2].view(torch.float16).view(S, TP_ELEMS)
         if name == "s_entry":
             return self.scratch[off:off + S * HEAD_DIM * HEAD_DIM * 2].view(torch.bfloat16).view(S, HEAD_DIM, HEAD_DIM)
         raise KeyError(name)

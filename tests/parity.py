@@ -7,9 +7,12 @@ Tolerances (written here once, used by every parity test):
     (bf16 storage alone is ~2^-9 relative)
   * gc: |err| <= 1e-4 * (1 + |G|)   (64 float32 additions)
   * decays exp(G_t), exp(G_{n-1} - G_t): relative error <= 1e-4
-  * T' (hi + lo bf16 pair, ~2^-17): relative Frobenius <= 1e-4 per slot; W and
-    U rebuilt from it (U = T' V, W = T' diag(exp(G)) K): <= 1e-4 against the
-    oracle's direct triangular solves
+  * T' (stored in float16, unit roundoff 2^-11 = 4.9e-4 per element, on top
+    of the solve's hi/lo products, <= 2^-16): relative Frobenius <= 6e-4 per
+    slot; W and U
+    rebuilt from it (U = T' V, W = T' diag(exp(G)) K): <= 1e-3 against the
+    oracle's direct triangular solves (the products may lose a little of the
+    per-element bound to cancellation)
 """
 
 import os
@@ -23,8 +26,8 @@ TOL_O_MAXABS = 2e-2
 TOL_STATE_RELFRO = 1e-3
 TOL_ENTRY_MAXABS = 2e-2
 TOL_ENTRY_RELFRO = 4e-3
-TOL_WU_RELFRO = 1e-4
-TOL_TP_RELFRO = 1e-4
+TOL_WU_RELFRO = 1e-3
+TOL_TP_RELFRO = 6e-4
 
 
 def relfro(a, b):
@@ -32,15 +35,15 @@ def relfro(a, b):
     return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
 
 
-# element offset of fragment f in a part, and whether it keeps only the first
-# 4 bf16 per lane (the diagonal fragments f = 0, 4, whose other half lies above
-# the diagonal)
+# element offset of fragment f, and whether it keeps only the first 4 values
+# per lane (the diagonal fragments f = 0, 4, whose other half lies above the
+# diagonal)
 _TP_OFF = (0, 256, 768, 1280, 1792, 2048)
 _TP_HALF = (True, False, False, False, True, False)
 
 
 def _tp_index():
-    """Row / column of each stored element of one T' part (2560 bf16): fragment
+    """Row / column of each stored element of a slot's T' (2560 values): fragment
     f of the six lower-triangular (mt, kb) (f = mt for kb = 0, f = mt + 2 for
     kb = 1), lane 16q + r holds row 16mt + r, columns 32kb + 4q + e and
     32kb + 16 + 4q + e; the diagonal fragments hold only the first four."""
@@ -64,12 +67,10 @@ def _tp_index():
 _TP_T, _TP_S = _tp_index()
 
 
-def unpack_tp(parts):
-    """T' [64, 64] from the documented layout [2][2560] (part 0 hi, part 1 lo);
-    elements not stored are 0."""
-    f = np.asarray(parts, dtype=np.float64)
+def unpack_tp(vals):
+    """T' [64, 64] from the documented layout [2560]; elements not stored are 0."""
     T = np.zeros((64, 64))
-    T[_TP_T, _TP_S] = f[0] + f[1]
+    T[_TP_T, _TP_S] = np.asarray(vals, dtype=np.float64)
     return T
 
 

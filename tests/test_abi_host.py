@@ -142,7 +142,7 @@ def test_scratch_layout_arithmetic():
     assert L.slots == slots and L.gc == 0
     assert L.dec == slots * 64 * 4
     assert L.tp == L.dec + slots * 2 * 64 * 4
-    assert L.s_entry == L.tp + slots * 2 * 2560 * 2
+    assert L.s_entry == L.tp + slots * 2560 * 2
     assert L.total == L.s_entry + slots * 128 * 128 * 2
     assert B.gdn_prefill_scratch_bytes(2, 0, 2, 4, 128, 128, B.gdn_varlen(P, P, 0, 0)) == 256
     # partial last chunk: T = 200 -> 4 chunks
