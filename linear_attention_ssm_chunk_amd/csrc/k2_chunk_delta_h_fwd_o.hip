@@ -175,10 +175,10 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     // two vertically stacked tiles are the chain-order A fragment (mt, kb).
     // Only the fragments of the row blocks mt in the bit mask are formed (the
     // caller passes Mask<bits>).
-    auto scores = [&](const Stage &S, u32x4 *A, auto mask_tag) {
+    auto scores = [&](const Stage &S, u32x4 *A, auto mask_tag) __attribute__((always_inline)) {
       constexpr int mask = decltype(mask_tag)::value;
       constexpr int top = (mask & 8) ? 3 : (mask & 4) ? 2 : (mask & 2) ? 1 : 0;
-      auto frag = [&](const u32x4 *T, int mt, int kb) {
+      auto frag = [&](const u32x4 *T, int mt, int kb) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
       };
       bf16x8 qf[16];
@@ -227,7 +227,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     if (role == 0) {
       // ---- Q, K rows; outputs --------------------------------------------
       u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
-      auto fetch = [&](int c) {
+      auto fetch = [&](int c) __attribute__((always_inline)) {
         const int nn = min(kChunk, s.len - c * kChunk);
         // chunk bases are wave-uniform; a lane adds a 32-bit offset (row
         // pitches are bounded so that 64 rows stay below 2^31 bytes)
@@ -244,7 +244,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
           kx[jr] = *reinterpret_cast<const u32x4 *>(kc + off);
         }
       };
-      auto stash = [&](Stage &S) {
+      auto stash = [&](Stage &S) __attribute__((always_inline)) {
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
           S.qr[row_slot(4 * jr + nrow, piece)] = qx[jr];
@@ -254,7 +254,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       // outputs of chunk co (tile co % 2): whole row segments of the
       // workgroup's columns
       const int64_t orow = int64_t(p.nv) * kDim;
-      auto store_out = [&](int co) {
+      auto store_out = [&](int co) __attribute__((always_inline)) {
         const int nn = min(kChunk, s.len - co * kChunk);
         char *oc = reinterpret_cast<char *>(p.out + (s.tok0 + int64_t(co) * kChunk) * orow + int64_t(h) * kDim + col0);
         const uint32_t opitch = uint32_t(orow) * 2u;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     u32x4 tx[2 * kTpFrags];  // T' of the chunk stashed next: bf16 hi (f), lo (6 + f)
     float d0 = 0.f, d1 = 0.f, gg = 0.f;
     u32x4 vx[kVPieces];
-    auto fetch = [&](int c) {
+    auto fetch = [&](int c) __attribute__((always_inline)) {
       const int64_t sl = slot_of(p, s, h, c);
       const char *tsrc = reinterpret_cast<const char *>(p.tp) + sl * kTpBytes;
 #pragma unroll
@@ -318,7 +318,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     };
     // float16 T' -> bf16 hi + lo, exactly: 11 significant bits leave at most
     // 3 for x - hi
-    auto decode = [&]() {
+    auto decode = [&]() __attribute__((always_inline)) {
       const SplitK sp;
 #pragma unroll
       for (int f = 0; f < kTpFrags; ++f) {
@@ -334,7 +334,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         tx[kTpFrags + f] = u32x4{lw[0], lw[1], lw[2], lw[3]};
       }
     };
-    auto stash = [&](Stage &S) {
+    auto stash = [&](Stage &S) __attribute__((always_inline)) {
 #pragma unroll
       for (int f = 0; f < 2 * kTpFrags; ++f) S.tp[f * 64 + lane] = tx[f];
       S.dec[lane] = d0;
@@ -383,10 +383,10 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   // LDS operand readers: row fragments of the Q / K tiles (rows 16mt + r16,
   // columns 32kb + 8q .. +7) and K^T fragments (rows dk = perm_dk(16m + r16),
   // tokens 32kb + chain order: two transposing reads of the K rows)
-  auto rfrag = [&](const u32x4 *T, int mt, int kb) {
+  auto rfrag = [&](const u32x4 *T, int mt, int kb) __attribute__((always_inline)) {
     return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
   };
-  auto ktfrag = [&](const Stage &S, int m, int kb) {
+  auto ktfrag = [&](const Stage &S, int m, int kb) __attribute__((always_inline)) {
     const int pc = 4 * (m >> 1) + (r16 & 3), hb = 8 * (m & 1);
     const int t0 = 32 * kb + 4 * q4 + (r16 >> 2);
     const u32x2 lo = read_tr(S.kr, row_slot(t0, pc) * 16 + hb);
@@ -412,7 +412,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   bf16x8 ub[2];    // its bf16(uc), chain order over tokens
   // chunk c-1's output, finished in step c from the score fragments af: O^T +=
   // uc^T A^T, then bf16 into the chunk's output tile (8 bytes per lane per tile)
-  auto finish_output = [&](int co, const bf16x8 (&af)[kTpFrags]) {
+  auto finish_output = [&](int co, const bf16x8 (&af)[kTpFrags]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -422,7 +422,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     for (int mt = 0; mt < 4; ++mt)
       *reinterpret_cast<u32x2 *>(ot + (16 * mt + r16) * kOPitch) = pack4_bf16(O[mt][0], O[mt][1], O[mt][2], O[mt][3]);
   };
-  auto load_scores = [&](int co, bf16x8 (&af)[kTpFrags]) {
+  auto load_scores = [&](int co, bf16x8 (&af)[kTpFrags]) __attribute__((always_inline)) {
 #pragma unroll
     for (int f = 0; f < kTpFrags; ++f) af[f] = __builtin_bit_cast(bf16x8, afb[co & 1][f * 64 + lane]);
   };
@@ -517,7 +517,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       th[tri_frag(mt, 0)] = __builtin_bit_cast(bf16x8, S.tp[tri_frag(mt, 0) * 64 + lane]);
       tl[tri_frag(mt, 0)] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + tri_frag(mt, 0)) * 64 + lane]);
     }
-    auto form_r = [&](int mt, f32x4 &R) {
+    auto form_r = [&](int mt, f32x4 &R) __attribute__((always_inline)) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const uint32_t pr = vv[mt][ii >> 1];
