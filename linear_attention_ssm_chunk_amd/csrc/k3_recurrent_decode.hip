@@ -1,7 +1,7 @@
 // Decode: one recurrent step of the gated delta rule per sequence -- the step
 // that follows a prefill, on the state the prefill leaves in place (page
 // "spark_model/layers/ops/ssm_gdn_a3.rs", gdn_prefill_fla's doc comment: the
-// final state is updated in place, one [nv, kd, vd] state per request).  For
+// final state is updated in place, one state per request).  For
 // each (sequence, v-head), with h the stored state ([dk][dv] = S^T), a =
 // exp(g) and k, q of the v-head's k-head:
 //   delta = beta (v - a h^T k)                (dv)

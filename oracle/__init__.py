@@ -23,7 +23,8 @@ Modules
 Conventions shared with the GPU library only through documentation:
 
 * state orientation: ``h[dk][dv]`` as the page's ``h_state`` comment gives it
-  ("one [nv,kd,vd] per request"), i.e. the transpose of the recurrence's S;
+  (one state per request, key dimension before value dimension), i.e. the
+  transpose of the recurrence's S;
 * GQA grouping (the pages are silent): v-head ``h`` reads k-head
   ``(h * nk) // nv`` -- parity unpinned, it is a convention;
 * no query scale (the recurrence's ``o_t = S_t q_t`` has none).

@@ -6,8 +6,8 @@ The page "spark_model/layers/ops/ssm_gdn_a3.rs" (doc comment of
 ``gdn_prefill_fla``) lists three stages:
 
 1. recompute_wu: the chunk-local cumulative log-gate ``gc``; the strictly
-   lower matrix ``L`` that shares its buffer with the key Gram matrix ("L
-   aliases the kk Gram (disjoint triangles)", comment above ``smem_wu``); the
+   lower matrix ``L``, which shares its buffer with the key Gram matrix, the
+   two in opposite triangles (comment above ``smem_wu``); the
    solves ``(I+L) U = beta V`` and ``(I+L) W = beta exp(gc) K``.  The same
    solves written as one matrix, the UT transform ``T' = (I+L)^-1 diag(beta)``
    (``U = T' V``, ``W = T' diag(exp(gc)) K``), is ``ut_transform``.
