@@ -15,12 +15,13 @@
 // inverse is [[A^-1, 0], [-D^-1 C A^-1, D^-1]].
 //   * lane t scans g;
 //   * the lower 10 16x16 tiles of K K^T on bf16 MFMA (K is exact in bf16) ->
-//     L (f32, LDS, one row-major tile each);
+//     L in registers, its four diagonal tiles also in LDS;
 //   * the four diagonal 16x16 tiles of T by f32 forward substitution, one lane
 //     per column of each (<= 120 FMAs per lane);
 //   * the off-diagonal tiles of the two diagonal 32x32 blocks, then the lower
-//     left 32x32 block, by the formula above on MFMA, every operand split
-//     into bf16 hi + lo (three products each, ~2^-17 relative error);
+//     left 32x32 block, by the formula above on MFMA, transposed, every
+//     operand split into bf16 hi + lo (three products each, ~2^-17 relative
+//     error);
 //   * T' = T diag(beta), rounded to float16 (11 significant bits: the spine
 //     splits each value exactly into bf16 hi + lo), in the A-operand fragment
 //     order of the spine: fragment f = tri_frag(mt, kb) (mt >= 2kb) holds, in
@@ -39,20 +40,22 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, const 
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Tiles of L / T: tile (mr, ms), ms <= mr, holds rows 16mr.., columns 16ms..
-// row-major with a pitch of kTP floats; tiles lie kTileF floats apart.  The
-// pitch puts the 4 rows x 16 columns a wave writes from a C fragment in 64
-// distinct banks; the extra 4 floats per tile put the four diagonal tiles,
-// which the substitution reads at once, in different banks.
+// LDS tiles: the four diagonal 16x16 tiles of L, overwritten by those of T,
+// and T's tile (1, 0); row-major with a pitch of kTP floats, kTileF floats
+// apart.  The pitch puts the 4 rows x 16 columns a wave writes from a C
+// fragment, or reads as a column fragment, in 64 distinct banks; the extra 4
+// floats per tile put the four diagonal tiles, which the substitution reads at
+// once, in different banks.  The off-diagonal tiles of L never leave the
+// registers they are formed in.
 constexpr int kTP = 20;
 constexpr int kTileF = 16 * kTP + 4;
 __host__ __device__ constexpr int tri_tile(int mr, int ms) { return mr * (mr + 1) / 2 + ms; }
 
-// LDS workspace of one solving wave (13.2 KB).
+// LDS workspace of one solving wave (6.9 KB).
 struct __align__(16) UtWork {
-  float L[10 * kTileF];
-  float Gs[kChunk]; // log2(e) G_t, for exp2
-  float Bs[kChunk]; // beta_t
+  float D[5 * kTileF]; // tiles 0..3: (b, b); tile 4: T(1, 0)
+  float Gs[kChunk];    // log2(e) G_t, for exp2
+  float Bs[kChunk];    // beta_t
 };
 
 // hi = bf16(x), lo = bf16(x - hi) for pairs of floats; x - hi is exact in
@@ -118,7 +121,14 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
                                          int lane, u32x4 (&tx)[kTpFrags], float &G, float &Gn) {
   const int q4 = lane >> 4, r16 = lane & 15;
   const SplitK sp;
-  auto tile = [&](int mr, int ms) -> float * { return W.L + tri_tile(mr, ms) * kTileF; };
+  auto dt = [&](int b) -> float * { return W.D + b * kTileF; };
+  // rows 4q .. 4q+3 of column r of an LDS tile (a C, or B, fragment)
+  auto col4 = [&](const float *T) -> f32x4 {
+    return f32x4{T[(4 * q4) * kTP + r16], T[(4 * q4 + 1) * kTP + r16], T[(4 * q4 + 2) * kTP + r16],
+                 T[(4 * q4 + 3) * kTP + r16]};
+  };
+  // columns 4q .. 4q+3 of row r of an LDS tile (an A fragment)
+  auto row4 = [&](const float *T) -> f32x4 { return *reinterpret_cast<const f32x4 *>(T + r16 * kTP + 4 * q4); };
 
   // ---- gate: inclusive prefix sum over the chunk ---------------------------
   G = gv;
@@ -131,7 +141,9 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
   W.Gs[lane] = G * 1.4426950408889634f; // log2(e) G, for exp2 below
   W.Bs[lane] = bv;
 
-  // ---- L = strict_lower(diag(beta) (D * K K^T)), tile by tile --------------
+  // ---- L = strict_lower(diag(beta) (D * K K^T)) as C fragments (lane: column
+  // 16ms + r, rows 16mr + 4q .. +3); the diagonal tiles go to LDS -----------
+  f32x4 lc[10];
 #pragma unroll
   for (int mr = 0; mr < 4; ++mr) {
     const f32x4 gr = *reinterpret_cast<const f32x4 *>(W.Gs + 16 * mr + 4 * q4);
@@ -141,13 +153,19 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) acc = mfma(kf[mr][kb], kf[ms][kb], acc);
-      const int sc = 16 * ms + r16; // C tile: column s, rows r
+      const int sc = 16 * ms + r16;
       const float gs = W.Gs[sc];
-      float *T = tile(mr, ms);
+      f32x4 l;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * mr + 4 * q4 + ii;
-        T[(4 * q4 + ii) * kTP + r16] = (sc < r) ? br[ii] * __builtin_amdgcn_exp2f(gr[ii] - gs) * acc[ii] : 0.f;
+        l[ii] = (sc < r) ? br[ii] * __builtin_amdgcn_exp2f(gr[ii] - gs) * acc[ii] : 0.f;
+      }
+      if (ms == mr) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) dt(mr)[(4 * q4 + ii) * kTP + r16] = l[ii];
+      } else {
+        lc[tri_tile(mr, ms)] = l;
       }
     }
   }
@@ -156,7 +174,7 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
   // tile (b, b):  T[r][j] = delta_rj - sum_{s<r} L[r][s] T[s][j] ------------
   {
     const int b = lane >> 4, jj = lane & 15;
-    float *D = W.L + (b * (b + 1) / 2 + b) * kTileF;
+    float *D = dt(b);
     float t[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -179,116 +197,91 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
     for (int rr = 0; rr < 16; ++rr) D[rr * kTP + jj] = t[rr];
   }
 
-  // ---- off-diagonal tiles of the two diagonal 32x32 blocks (e = 0, 1):
-  // T(2e+1, 2e) = -T(2e+1, 2e+1) (L(2e+1, 2e) T(2e, 2e)), 16x16x16 products
-  // (A: lane holds row r, columns 4q..4q+3; B: column r, rows 4q..4q+3; C
-  // likewise, so P's C fragment is the B operand of the second product) -----
-  {
-    f32x4 P[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(tile(2 * e + 1, 2 * e) + r16 * kTP + 4 * q4);
-      const float *Td = tile(2 * e, 2 * e);
-      const f32x4 bcol = {Td[(4 * q4 + 0) * kTP + r16], Td[(4 * q4 + 1) * kTP + r16], Td[(4 * q4 + 2) * kTP + r16],
-                          Td[(4 * q4 + 3) * kTP + r16]};
-      bf16x4 ah, al, bh, bl;
-      sp.four(a, ah, al);
-      sp.four(bcol, bh, bl);
-      P[e] = mfma16(ah, bh, zero4());
-      P[e] = mfma16(ah, bl, P[e]);
-      P[e] = mfma16(al, bh, P[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(tile(2 * e + 1, 2 * e + 1) + r16 * kTP + 4 * q4);
-      bf16x4 ah, al, ph, pl;
-      sp.four(a, ah, al);
-      sp.four(P[e], ph, pl);
-      f32x4 acc = mfma16(ah, ph, zero4());
-      acc = mfma16(ah, pl, acc);
-      acc = mfma16(al, ph, acc);
-      float *To = tile(2 * e + 1, 2 * e);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) To[(4 * q4 + ii) * kTP + r16] = -acc[ii];
-    }
-  }
+  // The remaining blocks are formed transposed: a C fragment read as an A
+  // operand is the transpose of its tile, so L's off-diagonal tiles serve as
+  // A operands where they are, and each result comes out with a lane holding
+  // four consecutive columns of one row -- the order of T''s fragments.
 
-  // ---- lower left 32x32 block: T21 = -T22 (L21 T11) -----------------------
-  {
-    // Pm = L21 T11 (16x16x32 products, contiguous k order: lane holds k =
-    // 8q .. 8q+7, inside tile column q / 2).  T11's columns are read from its
-    // rows; its upper right tile is zero and not stored.
-    const int kt = q4 >> 1, kr0 = 8 * (q4 & 1);
-    bf16x8 bh[2], bl[2];
+  // ---- off-diagonal tiles of the two diagonal 32x32 blocks (e = 0, 1):
+  // T(2e+1, 2e)^T = -T(2e, 2e)^T (L(2e+1, 2e)^T T(2e+1, 2e+1)^T) -------------
+  f32x4 Rt[2]; // Rt[e]: lane holds T(2e+1, 2e)[r][4q .. 4q+3]
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    bf16x4 ah, al, bh, bl;
+    sp.four(lc[tri_tile(2 * e + 1, 2 * e)], ah, al);  // L(2e+1, 2e)^T
+    sp.four(row4(dt(2 * e + 1)), bh, bl);             // T(2e+1, 2e+1)^T
+    f32x4 Q = mfma16(ah, bh, zero4());
+    Q = mfma16(ah, bl, Q);
+    Q = mfma16(al, bh, Q);
+    sp.four(col4(dt(2 * e)), ah, al);                 // T(2e, 2e)^T
+    bf16x4 qh, ql;
+    sp.four(Q, qh, ql);
+    f32x4 acc = mfma16(ah, qh, zero4());
+    acc = mfma16(ah, ql, acc);
+    acc = mfma16(al, qh, acc);
+    Rt[e] = -acc;
+  }
+  // T(1, 0) to LDS: its columns are an operand below
+  *reinterpret_cast<f32x4 *>(dt(4) + r16 * kTP + 4 * q4) = Rt[0];
+
+  // ---- lower left 32x32 block: T21^T = -T11^T (L21^T T22^T), 16x16x32
+  // products in chain order (k = 4q.. in the first tile, 16 + 4q.. in the
+  // second) ------------------------------------------------------------------
+  // Q2[mp][np] = L21^T T22^T; A: L21^T row tile mp = L's tiles (2, mp), (3, mp)
+  // as C fragments; B: T22 rows 16np + r, columns 4q.. of its two column tiles
+  bf16x8 t22h[2], t22l[2];
+  sp.eight(row4(dt(2)), zero4(), t22h[0], t22l[0]);
+  sp.eight(Rt[1], row4(dt(3)), t22h[1], t22l[1]);
+  f32x4 Q2[2][2];
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp) {
+    bf16x8 ah, al;
+    sp.eight(lc[tri_tile(2, mp)], lc[tri_tile(3, mp)], ah, al);
 #pragma unroll
     for (int np = 0; np < 2; ++np) {
-      const bool nz = (np <= kt); // tile (kt, np) lies on or below the diagonal
-      const float *bt = tile(nz ? kt : 1, np) + r16; // (1, 1): any stored tile
-      f32x4 x0, x1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x0[e] = nz ? bt[(kr0 + e) * kTP] : 0.f;
-        x1[e] = nz ? bt[(kr0 + 4 + e) * kTP] : 0.f;
-      }
-      sp.eight(x0, x1, bh[np], bl[np]);
+      f32x4 acc = mfma(ah, t22h[np], zero4());
+      acc = mfma(ah, t22l[np], acc);
+      Q2[mp][np] = mfma(al, t22h[np], acc);
     }
-    f32x4 Pm[2][2];
+  }
+  // T21^T[mt][np] = -T11^T Q2: A: T11 columns 16mt + r, rows 4q.. of its two
+  // row tiles (T(0, mt) and T(1, mt); T(0, 1) = 0); B: Q2's C tiles
+  bf16x8 qh[2], ql[2];
 #pragma unroll
-    for (int mp = 0; mp < 2; ++mp) {
-      const float *ar = tile(2 + mp, kt) + r16 * kTP + kr0;
-      bf16x8 ah, al;
-      sp.eight(*reinterpret_cast<const f32x4 *>(ar), *reinterpret_cast<const f32x4 *>(ar + 4), ah, al);
+  for (int np = 0; np < 2; ++np) sp.eight(Q2[0][np], Q2[1][np], qh[np], ql[np]);
+  f32x4 T21t[2][2]; // lane holds T21[16np + r][16mt + 4q .. +3]
 #pragma unroll
-      for (int np = 0; np < 2; ++np) {
-        f32x4 acc = mfma(ah, bh[np], zero4());
-        acc = mfma(ah, bl[np], acc);
-        Pm[mp][np] = mfma(al, bh[np], acc);
-      }
-    }
-    // T21 = -T22 Pm; Pm's C tiles are the B operand in chain order over the
-    // 32 rows of Pm (k = 4q.. in tile 0, 16 + 4q.. in tile 1), and T22's A
-    // fragment in chain order is columns 4q.. of its tiles (2 + mt, 2) and
-    // (2 + mt, 3) (the latter zero for mt = 0)
-    bf16x8 ph[2], pl[2];
+  for (int mt = 0; mt < 2; ++mt) {
+    bf16x8 ah, al;
+    sp.eight(mt == 0 ? col4(dt(0)) : zero4(), col4(mt == 0 ? dt(4) : dt(1)), ah, al);
 #pragma unroll
-    for (int np = 0; np < 2; ++np)
-      sp.eight(Pm[0][np], Pm[1][np], ph[np], pl[np]);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4 *>(tile(2 + mt, 2) + r16 * kTP + 4 * q4);
-      const f32x4 a1 = (mt == 1) ? *reinterpret_cast<const f32x4 *>(tile(3, 3) + r16 * kTP + 4 * q4) : zero4();
-      bf16x8 ah, al;
-      sp.eight(a0, a1, ah, al);
-#pragma unroll
-      for (int np = 0; np < 2; ++np) {
-        f32x4 acc = mfma(ah, ph[np], zero4());
-        acc = mfma(ah, pl[np], acc);
-        acc = mfma(al, ph[np], acc);
-        float *To = tile(2 + mt, np);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) To[(4 * q4 + ii) * kTP + r16] = -acc[ii];
-      }
+    for (int np = 0; np < 2; ++np) {
+      f32x4 acc = mfma(ah, qh[np], zero4());
+      acc = mfma(ah, ql[np], acc);
+      acc = mfma(al, qh[np], acc);
+      T21t[mt][np] = -acc;
     }
   }
 
-  // ---- T' = T diag(beta), float16, in fragment order ----------------------
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (2 * kb > mt) continue;
-      const int s0 = 32 * kb + 4 * q4;
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(tile(mt, 2 * kb) + r16 * kTP + 4 * q4) *
-                      *reinterpret_cast<const f32x4 *>(W.Bs + s0);
-      u32x4 out = {cvt_pk_f16(a[0], a[1]), cvt_pk_f16(a[2], a[3]), 0u, 0u};
-      if (2 * kb + 1 <= mt) { // else the second four columns lie above the diagonal
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(tile(mt, 2 * kb + 1) + r16 * kTP + 4 * q4) *
-                        *reinterpret_cast<const f32x4 *>(W.Bs + s0 + 16);
-        out[2] = cvt_pk_f16(b[0], b[1]);
-        out[3] = cvt_pk_f16(b[2], b[3]);
-      }
-      tx[tri_frag(mt, kb)] = out;
+  // ---- T' = T diag(beta), float16, in fragment order: fragment (mt, kb) is
+  // row 16mt + r, columns 32kb + 4q .. and 32kb + 16 + 4q .. ----------------
+  auto emit = [&](int f, int kb, const f32x4 &a, const f32x4 &b, bool two) {
+    const int s0 = 32 * kb + 4 * q4;
+    const f32x4 x = a * *reinterpret_cast<const f32x4 *>(W.Bs + s0);
+    u32x4 out = {cvt_pk_f16(x[0], x[1]), cvt_pk_f16(x[2], x[3]), 0u, 0u};
+    if (two) {
+      const f32x4 y = b * *reinterpret_cast<const f32x4 *>(W.Bs + s0 + 16);
+      out[2] = cvt_pk_f16(y[0], y[1]);
+      out[3] = cvt_pk_f16(y[2], y[3]);
     }
+    tx[f] = out;
+  };
+  emit(tri_frag(0, 0), 0, row4(dt(0)), zero4(), false);
+  emit(tri_frag(1, 0), 0, Rt[0], row4(dt(1)), true);
+  emit(tri_frag(2, 0), 0, T21t[0][0], T21t[1][0], true);
+  emit(tri_frag(3, 0), 0, T21t[0][1], T21t[1][1], true);
+  emit(tri_frag(2, 1), 1, row4(dt(2)), zero4(), false);
+  emit(tri_frag(3, 1), 1, Rt[1], row4(dt(3)), true);
 }
 
 } // namespace gdn
