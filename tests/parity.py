@@ -20,6 +20,7 @@ import os
 import numpy as np
 
 from oracle import gdn_chunked, gdn_recurrence, kv_head_map
+from oracle.chunked import chunk_cumsum, gram_strict_lower, ut_transform, wy_solve
 from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64
 
 TOL_O_MAXABS = 2e-2
@@ -122,28 +123,59 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
                     worst["entry_maxabs"] = max(worst["entry_maxabs"], float(np.abs(s_gpu - ent_ref[c, j]).max()))
                     worst["entry_relfro"] = max(worst["entry_relfro"], relfro(s_gpu, ent_ref[c, j]))
                 if intermediates:
-                    n = min(64, L - 64 * c)
                     d = inter[c]
-                    gc_gpu = regions["gc"][sl].cpu().numpy().astype(np.float64)
-                    G = d["gc"][:, j]
-                    worst["gc_err"] = max(worst["gc_err"], float((np.abs(gc_gpu[:n] - G) / (1 + np.abs(G))).max()))
-                    # rows past the end repeat the last value
-                    worst["gc_err"] = max(worst["gc_err"], float(np.abs(gc_gpu[n:] - G[-1]).max(initial=0)))
-                    dec = regions["dec"][sl].cpu().numpy().astype(np.float64)
-                    eg_ref = np.exp(G)
-                    dn_ref = np.exp(G[-1] - G)
-                    # relative, with an absolute floor below float32's normal range
-                    worst["dec_err"] = max(worst["dec_err"],
-                                           float((np.abs(dec[0, :n] - eg_ref) / (eg_ref + 1e-33)).max()),
-                                           float((np.abs(dec[1, :n] - dn_ref) / (dn_ref + 1e-33)).max()))
-                    Tp = unpack_tp(regions["tp"][sl].float().cpu().numpy())
-                    assert np.all(Tp[n:] == 0) and np.all(Tp[:, n:] == 0), "padded rows/columns of T' must be 0"
-                    Tp = Tp[:n, :n]
-                    worst["tp_relfro"] = max(worst["tp_relfro"], relfro(Tp, d["Tp"][j]))
-                    kk = arrs["k"][64 * c:64 * c + n, j]
-                    vv = arrs["v"][64 * c:64 * c + n, j]
-                    worst["w_relfro"] = max(worst["w_relfro"], relfro(Tp @ (np.exp(G)[:, None] * kk), d["W"][j]))
-                    worst["u_relfro"] = max(worst["u_relfro"], relfro(Tp @ vv, d["U"][j]))
+                    _compare_slot(regions, sl, d["gc"][:, j], d["Tp"][j], d["W"][j], d["U"][j],
+                                  arrs["k"][64 * c:64 * c + 64, j], arrs["v"][64 * c:64 * c + 64, j], worst)
+    if report is not None:
+        report.update(worst)
+    return worst
+
+
+def _compare_slot(regions, sl, G, Tp_ref, W_ref, U_ref, kk, vv, worst):
+    """Stage-1 intermediates of one slot (n = len(G) tokens) against the
+    oracle's: gc, the decays, T' (padded rows and columns exactly 0), and W, U
+    rebuilt from the GPU's T'."""
+    n = len(G)
+    gc_gpu = regions["gc"][sl].cpu().numpy().astype(np.float64)
+    worst["gc_err"] = max(worst["gc_err"], float((np.abs(gc_gpu[:n] - G) / (1 + np.abs(G))).max()))
+    # rows past the end repeat the last value
+    worst["gc_err"] = max(worst["gc_err"], float(np.abs(gc_gpu[n:] - G[-1]).max(initial=0)))
+    dec = regions["dec"][sl].cpu().numpy().astype(np.float64)
+    eg_ref = np.exp(G)
+    dn_ref = np.exp(G[-1] - G)
+    # relative, with an absolute floor below float32's normal range
+    worst["dec_err"] = max(worst["dec_err"],
+                           float((np.abs(dec[0, :n] - eg_ref) / (eg_ref + 1e-33)).max()),
+                           float((np.abs(dec[1, :n] - dn_ref) / (dn_ref + 1e-33)).max()))
+    Tp = unpack_tp(regions["tp"][sl].float().cpu().numpy())
+    assert np.all(Tp[n:] == 0) and np.all(Tp[:, n:] == 0), "padded rows/columns of T' must be 0"
+    Tp = Tp[:n, :n]
+    worst["tp_relfro"] = max(worst["tp_relfro"], relfro(Tp, Tp_ref))
+    kk, vv = kk[:n], vv[:n]
+    worst["w_relfro"] = max(worst["w_relfro"], relfro(Tp @ (np.exp(G)[:, None] * kk), W_ref))
+    worst["u_relfro"] = max(worst["u_relfro"], relfro(Tp @ vv, U_ref))
+
+
+def check_chunks(dp, p, i, heads, chunks, report=None):
+    """Stage-1 intermediates of the given chunks of sequence i and v-heads
+    ``heads``, each against the oracle's stage-1 functions on that chunk's
+    inputs alone (the intermediates depend on nothing else), so that chunks of
+    the longest sequences can be checked without running the oracle over the
+    whole sequence.  Returns a dict of worst errors."""
+    heads_l = list(heads)
+    arrs = seq_arrays(p, i, heads_l)
+    L = int(p.lengths[i])
+    regions = {r: dp.region(r) for r in ("gc", "dec", "tp")}
+    worst = dict(w_relfro=0.0, u_relfro=0.0, tp_relfro=0.0, dec_err=0.0, gc_err=0.0)
+    for c in chunks:
+        a, b = 64 * c, min(L, 64 * c + 64)
+        k_c, v_c, g_c, beta_c = arrs["k"][a:b], arrs["v"][a:b], arrs["g"][a:b], arrs["beta"][a:b]
+        G = chunk_cumsum(g_c)
+        Lm = gram_strict_lower(k_c, beta_c, G)
+        Tp = ut_transform(Lm, beta_c)
+        W, U = wy_solve(Lm, k_c, v_c, beta_c, G)
+        for j, h in enumerate(heads_l):
+            _compare_slot(regions, dp.slot(i, h, c), G[:, j], Tp[j], W[j], U[j], k_c[:, j], v_c[:, j], worst)
     if report is not None:
         report.update(worst)
     return worst
@@ -152,8 +184,9 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
 def assert_within(worst, intermediates=False, entries=True):
     if os.environ.get("GDN_PARITY_VERBOSE"):
         print("worst errors:", {k: float("%.3g" % v) for k, v in worst.items()}, flush=True)
-    assert worst["o_maxabs"] <= TOL_O_MAXABS, worst
-    assert worst["state_relfro"] <= TOL_STATE_RELFRO, worst
+    if "o_maxabs" in worst:
+        assert worst["o_maxabs"] <= TOL_O_MAXABS, worst
+        assert worst["state_relfro"] <= TOL_STATE_RELFRO, worst
     if entries:
         assert worst["entry_maxabs"] <= TOL_ENTRY_MAXABS, worst
         assert worst["entry_relfro"] <= TOL_ENTRY_RELFRO, worst

@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 
 from linear_attention_ssm_chunk_amd import inputs as I  # noqa: E402
 from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64  # noqa: E402
-from parity import assert_within, check_problem, relfro  # noqa: E402
+from parity import assert_within, check_chunks, check_problem, relfro  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -231,6 +231,16 @@ def test_full_workload_sampled(dev, index, samples):
             worst[key] = max(worst.get(key, 0.0), val)
     print(f"workload {index}: {worst}", flush=True)
     assert_within(worst)
+    # stage 1's intermediates of the first, a middle and the last chunk of
+    # each sampled (sequence, head), at the full size
+    inter = {}
+    for (i, h) in samples:
+        nch = int(p.cu_chunks[i + 1] - p.cu_chunks[i])
+        w = check_chunks(dp, p, i, [h], sorted({0, nch // 2, nch - 1}))
+        for key, val in w.items():
+            inter[key] = max(inter.get(key, 0.0), val)
+    print(f"workload {index} stage-1 chunks: {inter}", flush=True)
+    assert_within(inter, intermediates=True, entries=False)
 
 
 def test_slow_decay_long_carry(dev):
