@@ -69,3 +69,28 @@ def test_float16_tp_error_does_not_grow_with_length():
     short = _worst(_final_states(1024, 2, 0.02, ("exact", "float16")), "float16")
     long = _worst(_final_states(4096, 2, 0.02, ("exact", "float16")), "float16")
     assert long < 2 * short + 1e-5, (short, long)
+
+
+def test_tp_entries_stay_within_one_for_unit_keys():
+    """float16 holds |x| < 65504.  With unit-norm keys (the method normalises
+    them), beta <= 1 and no decay (decays <= 1 only shrink L), T' stays within
+    [-1, 1] over random, clustered, alternating and low-rank key sets."""
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for trial in range(200):
+        kind = trial % 4
+        if kind == 0:
+            K = rng.standard_normal((64, 128))
+        elif kind == 1:
+            K = rng.standard_normal((1, 128)) + 0.05 * rng.standard_normal((64, 128))
+        elif kind == 2:
+            sgn = np.where(np.arange(64) % 2, -1.0, 1.0)[:, None]
+            K = sgn * rng.standard_normal((1, 128)) + 0.05 * rng.standard_normal((64, 128))
+        else:
+            K = rng.standard_normal((64, 3)) @ rng.standard_normal((3, 128))
+        K /= np.linalg.norm(K, axis=1, keepdims=True)
+        beta = np.ones((64, 1)) if trial % 3 else rng.uniform(0, 1, (64, 1))
+        G = np.zeros((64, 1))
+        Tp = ut_transform(gram_strict_lower(K[:, None, :], beta, G), beta)
+        worst = max(worst, float(np.abs(Tp).max()))
+    assert worst <= 1.0 + 1e-9, worst
