@@ -66,6 +66,25 @@ def test_gqa_ratio3_heads_distinguishable(dev):
     assert_within(w, intermediates=True)
 
 
+@pytest.mark.parametrize("case", [
+    # (lengths, nk, nv, kwargs): chain counts (sequences x v-heads) that give
+    # the spine 1, 2 and 4 strips per workgroup on a 256-CU MI355X (up to 32,
+    # 33..64 and more than 64 chains), checked in full
+    ([200, 131], 2, 8, {}),                                  # 16 chains
+    ([130], 4, 40, {}),                                       # 40 chains, GQA 10
+    ([1, 63, 64, 65, 200], 3, 12, dict(state="table", ragged=True)),  # 60 chains, GQA 4
+    ([130, 130, 130], 8, 32, {}),                             # 96 chains
+    ([5, 140, 64, 97], 4, 24, dict(state="table", ragged=True)),      # 96 chains, ragged
+])
+def test_every_strip_layout_in_full(dev, case):
+    lens, nk, nv, kw = case
+    p = I.make_problem(lens, nk=nk, nv=nv, seed=31 + nv)
+    dp = run(dev, p, **kw)
+    w = check_problem(dp, p, intermediates=True)
+    print(f"{len(lens) * nv} chains: {w}", flush=True)
+    assert_within(w, intermediates=True)
+
+
 def test_ragged_with_state_table(dev):
     lens = [1, 64, 65, 130, 0, 77, 129, 3]
     p = I.make_problem(lens, nk=1, nv=2, seed=11)
