@@ -225,3 +225,14 @@ def test_decode_rejects_without_touching_the_gpu():
         B.gdn_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h_state"], 0, a["out"], a["B"], a["nk"],
                      a["nv"], 128, 128, a["strides"], 0)
     assert e.value.code == B.GDN_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises: there is no
+    other code path."""
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libgdn_prefill.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        B.gdn_prefill_scratch_bytes(1, 64, 1, 1, 128, 128)
+    with pytest.raises(ImportError):
+        B.gdn_decode_validate(P, P, P, P, P, P, 0, P, 1, 1, 1, 128, 128, B.gdn_strides(128, 128, 1))
