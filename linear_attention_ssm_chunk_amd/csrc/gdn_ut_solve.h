@@ -6,7 +6,7 @@
 // stage 1: the chunk-local cumulative log-gate gc and the WY/UT solves
 // (I+L) U = beta V, (I+L) W = beta exp(gc) K, with L sharing the key Gram
 // matrix's buffer (comment above smem_wu).  For the chunk's n <= 64 tokens
-// (lanes and rows past the sequence end carry g = beta = 0):
+// (lanes past the sequence end carry g = beta = 0):
 //   G_r    = sum_{j<=r} g_j
 //   L[r,s] = beta_r exp(G_r - G_s) (k_r . k_s)        (s < r, else 0)
 //   T'     = (I + L)^-1 diag(beta)                     (the UT transform)
@@ -94,16 +94,18 @@ struct SplitK {
 };
 
 // K rows of a chunk in the contiguous k order: kf[m][kb] = K[16m + r][32kb +
-// 8q .. +7], rows t >= n zero.
+// 8q .. +7].  Rows t >= n repeat row n-1: they only meet beta = 0 (their rows
+// of L) or the strict lower mask (their columns), so T' does not depend on
+// them, and the loads carry no condition that would make them wait on one
+// another.
 __device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[4][4], const uint16_t *kbase, int64_t qk_row, int n,
                                              int lane) {
   const int q4 = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int t = 16 * m + r16;
+    const int t = min(16 * m + r16, n - 1);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      kf[m][kb] = (t < n) ? load16_bf16x8(kbase + int64_t(t) * qk_row + 32 * kb + 8 * q4) : zero8();
+    for (int kb = 0; kb < 4; ++kb) kf[m][kb] = load16_bf16x8(kbase + int64_t(t) * qk_row + 32 * kb + 8 * q4);
   }
 }
 
