@@ -28,9 +28,9 @@
 //     active pair stages chunk c+1 into the free half of a double-buffered
 //     LDS stage, from registers it filled two steps earlier, then fetches
 //     chunk c+3: role 0 the Q and K rows (1 KB per load), role 1 the T'
-//     fragments (float16), decays, gate sums and V rows.  The idle pair works
-//     on chunk c, visible in the stage compute reads: role 1 splits the T' it
-//     fetched last into bf16 hi + lo, reads the Q and K row fragments and
+//     fragments (float16, split into bf16 hi + lo as they are staged),
+//     decays, gate sums and V rows.  The idle pair works on chunk c, visible
+//     in the stage compute reads: role 1 reads the Q and K row fragments and
 //     forms the causal decayed scores A of chunk c on MFMA (for S = 4 role 0
 //     forms half of them); role 0 stores the output tile of chunk c-2.
 //     The compute waves read K^T and their V tiles out of the row tiles with
@@ -288,8 +288,8 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     }
 
     // ---- T', decays, gate sums, V rows; scores ------------------------------
-    u32x4 t16[kTpFrags];     // T' of the chunk fetched last, float16
-    u32x4 tx[2 * kTpFrags];  // T' of the chunk stashed next: bf16 hi (f), lo (6 + f)
+    u32x4 t16[kTpFrags];     // T' as fetched, float16
+    u32x4 tx[2 * kTpFrags];  // T' as staged: bf16 hi (f), lo (6 + f)
     float d0 = 0.f, d1 = 0.f, gg = 0.f;
     u32x4 vx[kVPieces];
     auto fetch = [&](int c) __attribute__((always_inline)) {
@@ -343,23 +343,22 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
       for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
-    if (pair < nch) {
-      fetch(pair);
-      decode();
-    }
+    if (pair < nch) fetch(pair);
     if (pair == 0) {
+      decode();
       stash(st[0]);
       if (2 < nch) fetch(2);
     }
     __syncthreads();
     for (int c = 0; c <= nch; ++c) {
+      // the active pair splits the T' it fetched two steps earlier and
+      // stages chunk c+1
       if (((c + 1) & 1) == pair && c + 1 < nch) {
+        decode();
         stash(st[(c + 1) & 1]);
         if (c + 3 < nch) fetch(c + 3);
       }
-      // the idle pair splits the T' it fetched last (chunk c+2, stashed in
-      // step c+1) and forms the scores of chunk c (with role 0 for S = 4)
-      if ((c & 1) == pair && c + 2 < nch) decode();
+      // the idle pair forms the scores of chunk c (with role 0 for S = 4)
       if ((c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<kStrips == 4 ? 0x6 : 0xF>());
       __syncthreads();
     }
