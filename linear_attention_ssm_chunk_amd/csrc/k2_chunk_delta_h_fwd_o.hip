@@ -546,6 +546,15 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       th[tri_frag(mt, 1)] = __builtin_bit_cast(bf16x8, S.tp[tri_frag(mt, 1) * 64 + lane]);
       tl[tri_frag(mt, 1)] = __builtin_bit_cast(bf16x8, S.tp[(kTpFrags + tri_frag(mt, 1)) * 64 + lane]);
     }
+    // the decays of uc and of the output's state term, two sections ahead of
+    // their use
+    f32x4 dn[4];
+    float dq[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      dn[mt] = *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
+      dq[mt] = S.dec[16 * mt + r16];
+    }
     f32x4 D[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -573,10 +582,10 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     bf16x8 Dh[2], Dl[2];
     ub[0] = chain_frag(D[0], D[1]);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) D[mt] *= *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
+    for (int mt = 0; mt < 2; ++mt) D[mt] *= dn[mt];
     split_tiles(D[0], D[1], m0, m1, Dh[0], Dl[0]);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) O[mt] *= S.dec[16 * mt + r16];
+    for (int mt = 0; mt < 4; ++mt) O[mt] *= dq[mt];
     GDN_INTERLEAVE(6, 6, 4);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -592,7 +601,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     }
     ub[1] = chain_frag(D[2], D[3]);
 #pragma unroll
-    for (int mt = 2; mt < 4; ++mt) D[mt] *= *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
+    for (int mt = 2; mt < 4; ++mt) D[mt] *= dn[mt];
     split_tiles(D[2], D[3], m0, m1, Dh[1], Dl[1]);
     GDN_INTERLEAVE(16, 2, 5);
     __builtin_amdgcn_sched_barrier(0);
