@@ -30,8 +30,8 @@
  *     as the page's tile guard gdn_tc_spine_reject is); other sizes are
  *     rejected with GDN_EUNSUPPORTED.
  *   - GQA grouping: v-head h reads k-head (h * nk) / nv; nv % nk == 0.
- *   - The state is stored h[dk][dv] (the page's "[nv,kd,vd]" h_state), the
- *     transpose of S above.
+ *   - The state is stored h[dk][dv] (as the page's h_state: nv states per
+ *     request, key dimension first), the transpose of S above.
  *   - Tokens of a sequence occupy consecutive token rows.  Dense mode:
  *     sequence b is rows b*T .. b*T+T-1.  Ragged mode: rows cu_seqlens[i] ..
  *     cu_seqlens[i+1]-1.
@@ -44,6 +44,10 @@
  *   - exp(gc) of the chunk-local gate must stay finite in float32 (gc < 88);
  *     g <= 0 (a decay) always satisfies it, and any decay however strong is
  *     handled (factors that underflow are 0, as they are in the result).
+ *   - Keys are expected to be unit-norm (the method L2-normalises q and k)
+ *     and beta in [0, 1]: T' passes between the kernels in float16, whose
+ *     range then holds it (|T'| <= 1); keys far from unit norm can overflow
+ *     it.
  *
  * Ownership.  The caller owns every buffer.  The library allocates nothing,
  * keeps no pointer after return, and never reads device memory from the host.
