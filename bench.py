@@ -3,10 +3,10 @@
     python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--workload 3]
 
 One step = one gdn_prefill call (both kernels: stage 1, then the spine with the
-output fused in) over the whole synthetic workload, inputs resident in HBM.  Default workload: B=4 sequences of T=8192
-tokens, nk=16 k-heads, nv=32 v-heads, dk=dv=128, carried float32 state updated
-in place, per-chunk entry states emitted (the T=8192 workload the target is
-stated on).  Prints one JSON line.
+output fused in) over the whole synthetic workload, inputs resident in HBM.
+Default workload: B=4 sequences of T=8192 tokens, nk=16 k-heads, nv=32
+v-heads, dk=dv=128, carried float32 state updated in place, per-chunk entry
+states emitted.  Prints one JSON line.
 
 Warm-up: the W untimed warm-up steps run first; if they took less than 50 ms
 of GPU time, untimed steps continue until 50 ms have passed.  An idle MI355X

@@ -43,6 +43,7 @@ class DeviceProblem:
         self.nseq, self.nk, self.nv = p.nseq, p.nk, p.nv
         self.N = p.n_tokens
         lens = p.lengths
+        self._chunk0 = p.cu_chunks  # chunk offsets, computed once (slot() reads them per slot)
         self.ragged = (len(set(lens)) != 1) if ragged is None else bool(ragged)
         if not self.ragged and lens[0] == 0:
             raise ValueError("dense mode needs T > 0")
@@ -106,7 +107,11 @@ class DeviceProblem:
 
     # -- state ---------------------------------------------------------------
     def reset_state(self):
-        h0 = torch.from_numpy(np.ascontiguousarray(self.p.h0))
+        h0 = self.p.h0
+        if hasattr(h0, "to_torch"):  # initial states that build themselves on the device
+            h0 = h0.to_torch(self.device)
+        else:
+            h0 = torch.from_numpy(np.ascontiguousarray(h0))
         if self.state_kind == "contiguous":
             self.h.copy_(h0)
         else:
@@ -117,6 +122,10 @@ class DeviceProblem:
         if self.state_kind == "contiguous":
             return self.h.cpu().numpy()
         return np.stack([t.cpu().numpy() for t in self.h_list])
+
+    def state_of(self, i):
+        """The state [nv][128][128] of sequence i, copied to the host."""
+        return (self.h[i] if self.state_kind == "contiguous" else self.h_list[i]).cpu().numpy()
 
     # -- calls ---------------------------------------------------------------
     def args(self):
@@ -174,6 +183,6 @@ class DeviceProblem:
 
     def slot(self, i, h, c):
         """Slot index of (sequence i, v-head h, chunk c)."""
-        chunk0 = int(self.p.cu_chunks[i])
-        nch = int(self.p.cu_chunks[i + 1] - self.p.cu_chunks[i])
+        chunk0 = int(self._chunk0[i])
+        nch = int(self._chunk0[i + 1]) - chunk0
         return chunk0 * self.nv + h * nch + c

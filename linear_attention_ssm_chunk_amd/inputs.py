@@ -155,6 +155,8 @@ def make_problem(lengths, nk, nv, seed, h0="normal"):
     if h0 == "normal":
         h = (0.02 * np.random.default_rng(ss[5]).standard_normal((nseq, nv, HEAD_DIM, HEAD_DIM),
                                                                  dtype=np.float32)).astype(np.float32)
+    elif h0 == "none":  # the caller sets p.h0
+        h = None
     else:
         h = np.zeros((nseq, nv, HEAD_DIM, HEAD_DIM), dtype=np.float32)
     return Problem(list(lengths), nk, nv, q, k, v, g, beta, h, seed)

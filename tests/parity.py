@@ -75,10 +75,12 @@ def unpack_tp(vals):
     return T
 
 
-def seq_arrays(p, i, heads=None):
+def seq_arrays(p, i, heads=None, cu=None):
     """Oracle inputs of sequence i restricted to v-heads ``heads``; the k-heads
-    are selected with the documented grouping so the oracle sees nk = nv."""
-    a, b = int(p.cu_seqlens[i]), int(p.cu_seqlens[i + 1])
+    are selected with the documented grouping so the oracle sees nk = nv.
+    ``cu``: p.cu_seqlens, when the caller already holds it."""
+    cu = p.cu_seqlens if cu is None else cu
+    a, b = int(cu[i]), int(cu[i + 1])
     heads = list(range(p.nv)) if heads is None else list(heads)
     kap = kv_head_map(p.nk, p.nv)[heads]
     return dict(q=bf16_to_f64(p.q[a:b][:, kap]), k=bf16_to_f64(p.k[a:b][:, kap]),
@@ -92,7 +94,6 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
     seqs = range(p.nseq) if seqs is None else seqs
     heads_l = list(range(p.nv)) if heads is None else list(heads)
     out = dp.output()
-    state = dp.state()
     worst = dict(o_maxabs=0.0, state_relfro=0.0, entry_maxabs=0.0, entry_relfro=0.0,
                  w_relfro=0.0, u_relfro=0.0, tp_relfro=0.0, dec_err=0.0, gc_err=0.0)
     regions = {}
@@ -101,10 +102,11 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
     if intermediates:
         for r in ("gc", "dec", "tp"):
             regions[r] = dp.region(r)
+    cu = p.cu_seqlens
     for i in seqs:
-        a = int(p.cu_seqlens[i])
+        a = int(cu[i])
         L = int(p.lengths[i])
-        arrs = seq_arrays(p, i, heads_l)
+        arrs = seq_arrays(p, i, heads_l, cu)
         if intermediates:
             o_ref, h_ref, ent_ref, inter = gdn_chunked(**arrs, keep_intermediates=True)
         else:
@@ -112,8 +114,9 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
         if L:
             o_gpu = out[a:a + L][:, heads_l]
             worst["o_maxabs"] = max(worst["o_maxabs"], float(np.abs(o_gpu - o_ref).max()))
+        state_i = dp.state_of(i)
         for j, h in enumerate(heads_l):
-            e = relfro(state[i][h].astype(np.float64), h_ref[j])
+            e = relfro(state_i[h].astype(np.float64), h_ref[j])
             worst["state_relfro"] = max(worst["state_relfro"], e)
             for c in range(ent_ref.shape[0]):
                 sl = dp.slot(i, h, c)

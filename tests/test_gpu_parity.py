@@ -102,6 +102,82 @@ def test_all_sequences_empty(dev):
     assert np.array_equal(dp.state(), p.h0)
 
 
+class _DistinctH0:
+    """Initial states h0[i] = base[i % 61] * scale[i], scale[i] = float32(1 +
+    i / nseq), distinct per sequence: built on the device in one pass rather
+    than drawn and uploaded whole; h0[i] gives sequence i's on the host (the
+    same float32 products)."""
+
+    def __init__(self, nseq, nv, seed):
+        self.base = 0.02 * np.random.default_rng(seed).standard_normal((61, nv, 128, 128), dtype=np.float32)
+        self.scale = (1.0 + np.arange(nseq) / nseq).astype(np.float32)
+        self.shape = (nseq, nv, 128, 128)
+
+    def __getitem__(self, i):
+        return self.base[i % 61] * self.scale[i]
+
+    def to_torch(self, device):
+        idx = torch.arange(self.shape[0], device=device) % 61
+        return torch.from_numpy(self.base).to(device)[idx] * torch.from_numpy(self.scale).to(device)[:, None, None, None]
+
+
+def _edge_sample(nseq, extra, n_random, seed):
+    """The first and last 300 sequences, the indices in ``extra`` and
+    ``n_random`` drawn at random."""
+    drawn = np.random.default_rng(seed).choice(nseq, n_random, replace=False).tolist()
+    return sorted(set(range(300)) | set(range(nseq - 300, nseq)) | set(extra) | set(drawn))
+
+
+MAX_B = 65535  # the largest batch the boundary accepts (one grid row per sequence)
+
+
+def test_largest_batch_ragged(dev):
+    """B = 65535 ragged sequences, mostly of 0-3 tokens, with sequences of one
+    to three chunks at both ends and in the middle.  Every empty sequence keeps
+    its state bit for bit; a sample (both ends, the long ones, 1500 at random)
+    against the oracle, entry states included."""
+    lens = [(0, 1, 2, 3)[i % 4] for i in range(MAX_B)]
+    long_ = {0: 130, 1: 65, 32768: 192, MAX_B - 3: 64, MAX_B - 1: 129}
+    for i, L in long_.items():
+        lens[i] = L
+    p = I.make_problem(lens, nk=1, nv=1, seed=750, h0="none")
+    p.h0 = _DistinctH0(MAX_B, 1, 751)
+    print(f"[gpu] ragged B={MAX_B} nk=1 nv=1", flush=True)
+    dp = dev(p, ragged=True)
+    h_init = dp.h.clone()
+    dp.run()
+    torch.cuda.synchronize()
+    empty = torch.from_numpy(np.flatnonzero(np.asarray(lens) == 0)).to(dp.h.device)
+    assert torch.equal(dp.h[empty], h_init[empty])
+    del h_init
+    w = check_problem(dp, p, seqs=_edge_sample(MAX_B, long_, 1500, 752))
+    print(w, flush=True)
+    assert_within(w)
+
+
+def test_largest_batch_decode(dev):
+    """One decode step for B = 65535 sequences (GQA 2): a sample (both ends,
+    1500 at random) against the oracle recurrence."""
+    from oracle import gdn_recurrence
+    from parity import seq_arrays
+    p = I.make_problem([1] * MAX_B, nk=1, nv=2, seed=760, h0="none")
+    p.h0 = _DistinctH0(MAX_B, 2, 761)
+    print(f"[gpu] decode B={MAX_B} nk=1 nv=2", flush=True)
+    dp = dev(p, ragged=False)
+    dp.decode_step(0)
+    torch.cuda.synchronize()
+    out = dp.dec_out.float().cpu().numpy()
+    cu = p.cu_seqlens
+    o_err = s_err = 0.0
+    for i in _edge_sample(MAX_B, (), 1500, 762):
+        o_ref, h_ref, _ = gdn_recurrence(**seq_arrays(p, i, cu=cu))
+        st = dp.state_of(i).astype(np.float64)
+        o_err = max(o_err, float(np.abs(out[i] - o_ref[0]).max()))
+        s_err = max(s_err, max(relfro(st[h], h_ref[h]) for h in range(p.nv)))
+    print(f"decode B={MAX_B}: o_maxabs={o_err:.3g} state_relfro={s_err:.3g}", flush=True)
+    assert o_err <= 2e-2 and s_err <= 1e-5
+
+
 def test_packed_conv_layout_bit_identical(dev):
     p = I.make_problem([200, 200], nk=2, nv=6, seed=13)
     a = run(dev, p, layout="contiguous")
