@@ -166,6 +166,12 @@ class DeviceProblem:
     def output(self):
         return _bf16_tensor_to_f32(self.out)
 
+    def output_rows(self, a, b, heads):
+        """Output rows a..b-1 of the v-heads ``heads`` as float32, copied to
+        the host without converting the rest."""
+        idx = torch.as_tensor(list(heads), device=self.out.device)
+        return _bf16_tensor_to_f32(self.out[a:b].index_select(1, idx))
+
     def region(self, name):
         """A scratch region as a torch view shaped [slots, ...]."""
         L = self.layout_info

@@ -93,7 +93,6 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
     ``dp`` (output, final state, scratch).  Returns a dict of worst errors."""
     seqs = range(p.nseq) if seqs is None else seqs
     heads_l = list(range(p.nv)) if heads is None else list(heads)
-    out = dp.output()
     worst = dict(o_maxabs=0.0, state_relfro=0.0, entry_maxabs=0.0, entry_relfro=0.0,
                  w_relfro=0.0, u_relfro=0.0, tp_relfro=0.0, dec_err=0.0, gc_err=0.0)
     regions = {}
@@ -112,7 +111,7 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
         else:
             o_ref, h_ref, ent_ref = gdn_recurrence(**arrs)
         if L:
-            o_gpu = out[a:a + L][:, heads_l]
+            o_gpu = dp.output_rows(a, a + L, heads_l)
             worst["o_maxabs"] = max(worst["o_maxabs"], float(np.abs(o_gpu - o_ref).max()))
         state_i = dp.state_of(i)
         for j, h in enumerate(heads_l):

@@ -178,6 +178,24 @@ def test_largest_batch_decode(dev):
     assert o_err <= 2e-2 and s_err <= 1e-5
 
 
+def test_offsets_past_2_31(dev):
+    """One sequence of 140000 tokens (a ragged tail), nk=16, nv=64: the last
+    heads' entry states lie past 2^31 elements into the scratch and the
+    output's last rows past 2^31 bytes.  The last v-head (k-head 15, the far
+    end of the scratch) against the oracle over the whole sequence, stage 1's
+    intermediates at both ends and the middle of it."""
+    p = I.make_problem([140000], nk=16, nv=64, seed=770)
+    dp = run(dev, p)
+    last = dp.slot(0, 63, 2187)
+    assert last * 128 * 128 >= 2 ** 31 and 140000 * 64 * 128 * 2 >= 2 ** 31
+    w = check_problem(dp, p, heads=[63])
+    print(w, flush=True)
+    assert_within(w)
+    wc = check_chunks(dp, p, 0, [63], [0, 1093, 2187])
+    print(wc, flush=True)
+    assert_within(wc, intermediates=True, entries=False)
+
+
 def test_packed_conv_layout_bit_identical(dev):
     p = I.make_problem([200, 200], nk=2, nv=6, seed=13)
     a = run(dev, p, layout="contiguous")
