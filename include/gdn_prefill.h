@@ -166,7 +166,10 @@ int gdn_prefill_validate(const void *q, const void *k, const void *v, const floa
  *               the final state.  h_state_is_table == 0: contiguous
  *               [B][nv][dk][dv].  == 1: a device array of B device pointers,
  *               entry i -> [nv][dk][dv] of sequence i (the page's pointer
- *               table, one state per request).
+ *               table, one state per request).  The entries live in device
+ *               memory, so no call can check them: each must point to
+ *               nv*dk*dv writable floats (4-byte aligned) that no other entry
+ *               overlaps; the entry of a length-0 sequence is never read.
  *   out         bf16 [N_tok][nv][dv].
  *   scratch     device buffer of >= gdn_prefill_scratch_bytes(...) bytes; on
  *               return it holds the intermediates in the documented layout
@@ -223,7 +226,8 @@ int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *
  *   v        bf16; head h at v + b*v_row + h*128.
  *   g, beta  float at g[b*gb_row + h], beta[b*gb_row + h].
  *   h_state  as for gdn_prefill (contiguous [B][nv][dk][dv], or a device
- *            table of B pointers to [nv][dk][dv]), updated in place.
+ *            table of B pointers to [nv][dk][dv], each entry as there; every
+ *            entry is read), updated in place.
  *   out      bf16 [B][nv][dv], contiguous.
  * dk = dv = 128; 1 <= B <= 65535; nv * 256 < 2^32 (work-items of the launch).  No scratch; one launch on `stream`, no synchronisation.
  * Returns GDN_OK or an error as gdn_prefill does; gdn_decode_validate runs the
