@@ -38,14 +38,9 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-__device__ __forceinline__ bf16x8 zero8() {
-  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-}
-
 // float -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
@@ -53,16 +48,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
-// Split two floats into hi = bf16(x) and lo = bf16(x - hi), packed in pairs:
-// hi + lo carries about 16 mantissa bits, so a product of split operands done
-// as hi*hi + hi*lo + lo*hi keeps ~2^-17 relative error with bf16 MFMA.
-__device__ __forceinline__ void split_pk(float a, float b, uint32_t &hi, uint32_t &lo) {
-  hi = cvt_pk(a, b);
-  const float ha = __builtin_bit_cast(float, hi << 16);
-  const float hb = __builtin_bit_cast(float, hi & 0xFFFF0000u);
-  lo = cvt_pk(a - ha, b - hb);
-}
-
 // Pack four floats (consecutive elements of one lane) as 4 bf16 = 8 bytes.
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
   return u32x2{cvt_pk(a, b), cvt_pk(c, d)};
@@ -72,22 +57,6 @@ __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) 
 __device__ __forceinline__ bf16x8 chain_frag(const f32x4 &lo_tile, const f32x4 &hi_tile) {
   return __builtin_bit_cast(bf16x8, u32x4{cvt_pk(lo_tile[0], lo_tile[1]), cvt_pk(lo_tile[2], lo_tile[3]),
                                           cvt_pk(hi_tile[0], hi_tile[1]), cvt_pk(hi_tile[2], hi_tile[3])});
-}
-
-// Split eight floats into hi/lo bf16 fragments (see split_pk).
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) split_pk(x[2 * e], x[2 * e + 1], h[e], l[e]);
-  hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
-  lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
-}
-
-// Chain-order split fragment from two C tiles.
-__device__ __forceinline__ void chain_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi,
-                                            bf16x8 &lo) {
-  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-  split8(x, hi, lo);
 }
 
 // The dk order of the spine.  Row rho = 16m + 4q + i of the state tiles
@@ -105,12 +74,6 @@ __host__ __device__ constexpr int tri_frag(int mt, int kb) { return kb == 0 ? mt
 
 __device__ __forceinline__ bf16x8 load16_bf16x8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
-}
-__device__ __forceinline__ u32x2 load8(const uint16_t *p) {
-  return *reinterpret_cast<const u32x2 *>(p);
-}
-__device__ __forceinline__ bf16x8 join8(const u32x2 &a, const u32x2 &b) {
-  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
 // Where a sequence lives.  Ragged offsets are checked here so that a bad table
