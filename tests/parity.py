@@ -88,9 +88,13 @@ def seq_arrays(p, i, heads=None, cu=None):
                 beta=p.beta[a:b][:, heads].astype(np.float64), h0=p.h0[i][heads].astype(np.float64))
 
 
-def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=True, report=None):
+def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=True, report=None,
+                  chunked=False):
     """Run the oracle on (seqs x heads) and compare with what the GPU left in
-    ``dp`` (output, final state, scratch).  Returns a dict of worst errors."""
+    ``dp`` (output, final state, scratch).  The oracle is the token recurrence,
+    or its chunk form when ``chunked`` or ``intermediates`` is set (the two
+    agree to 1e-12, a CPU pin; the chunk form runs many heads of a long
+    sequence several times faster).  Returns a dict of worst errors."""
     seqs = range(p.nseq) if seqs is None else seqs
     heads_l = list(range(p.nv)) if heads is None else list(heads)
     worst = dict(o_maxabs=0.0, state_relfro=0.0, entry_maxabs=0.0, entry_relfro=0.0,
@@ -108,6 +112,8 @@ def check_problem(dp, p, seqs=None, heads=None, intermediates=False, entries=Tru
         arrs = seq_arrays(p, i, heads_l, cu)
         if intermediates:
             o_ref, h_ref, ent_ref, inter = gdn_chunked(**arrs, keep_intermediates=True)
+        elif chunked:
+            o_ref, h_ref, ent_ref, _ = gdn_chunked(**arrs)
         else:
             o_ref, h_ref, ent_ref = gdn_recurrence(**arrs)
         if L:

@@ -356,6 +356,22 @@ def test_full_workload_sampled(dev, index, samples):
     assert_within(inter, intermediates=True, entries=False)
 
 
+def test_batched_workload_every_chain(dev):
+    """The batched workload at full size (B=4, T=8192, nk=16, nv=32, carried
+    state; the launch the bench times): every (sequence, head) chain's
+    outputs, final state and all 128 entry states against the oracle's chunk
+    form."""
+    p = I.make_workload(3)
+    dp = run(dev, p)
+    worst = {}
+    for i in range(p.nseq):
+        w = check_problem(dp, p, seqs=[i], chunked=True)
+        print(f"sequence {i}: {w}", flush=True)
+        for key, val in w.items():
+            worst[key] = max(worst.get(key, 0.0), val)
+    assert_within(worst)
+
+
 def test_slow_decay_long_carry(dev):
     """g * 0.01 keeps the state alive across many chunks, so a state that is
     not carried (or carried wrongly) between chunks shows in every output."""

@@ -72,3 +72,60 @@ def test_planted_mistake_fails(problem):
     assert w["tp_relfro"] > 10 * TOL_TP_RELFRO
     with pytest.raises(AssertionError):
         assert_within(w, intermediates=True, entries=False)
+
+
+class ResultsFromOracle:
+    """Stand-in for DeviceProblem's results: outputs, final states and entry
+    states ([dv][dk], bf16) as the oracle's recurrence gives them, in the
+    documented layouts; ``plant="state_t"`` stores each final state
+    transposed."""
+
+    def __init__(self, p, plant=None):
+        from oracle import gdn_recurrence
+        self.p = p
+        self._cu_chunks = p.cu_chunks
+        nslots = int(self._cu_chunks[-1]) * p.nv
+        self.out = np.zeros((p.n_tokens, p.nv, 128), np.float32)
+        self.h = np.zeros((p.nseq, p.nv, 128, 128), np.float32)
+        ent = torch.zeros((nslots, 128, 128), dtype=torch.bfloat16)
+        cu = p.cu_seqlens
+        for i in range(p.nseq):
+            o, hf, e = gdn_recurrence(**seq_arrays(p, i))
+            self.out[cu[i]:cu[i + 1]] = o
+            self.h[i] = np.swapaxes(hf, 1, 2) if plant == "state_t" else hf
+            for hh in range(p.nv):
+                for c in range(e.shape[0]):
+                    ent[self.slot(i, hh, c)] = torch.from_numpy(e[c, hh].T.astype(np.float32))
+        self._ent = ent
+
+    def output_rows(self, a, b, heads):
+        return self.out[a:b][:, list(heads)]
+
+    def state_of(self, i):
+        return self.h[i]
+
+    def region(self, name):
+        assert name == "s_entry"
+        return self._ent
+
+    def slot(self, i, h, c):
+        chunk0 = int(self._cu_chunks[i])
+        nch = int(self._cu_chunks[i + 1]) - chunk0
+        return chunk0 * self.p.nv + h * nch + c
+
+
+@pytest.mark.parametrize("chunked", [False, True])
+def test_check_problem_passes_oracle_results(problem, chunked):
+    from parity import check_problem
+    w = check_problem(ResultsFromOracle(problem), problem, chunked=chunked)
+    assert_within(w)
+    # only the float32 / bf16 storage of the stand-in remains
+    assert w["o_maxabs"] < 1e-5 and w["state_relfro"] < 1e-6 and w["entry_relfro"] <= 2.0 ** -8
+
+
+def test_check_problem_rejects_transposed_state(problem):
+    from parity import TOL_STATE_RELFRO, check_problem
+    w = check_problem(ResultsFromOracle(problem, plant="state_t"), problem, seqs=[0], heads=[1])
+    assert w["state_relfro"] > 10 * TOL_STATE_RELFRO
+    with pytest.raises(AssertionError):
+        assert_within(w)
