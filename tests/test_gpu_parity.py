@@ -356,12 +356,13 @@ def test_full_workload_sampled(dev, index, samples):
     assert_within(inter, intermediates=True, entries=False)
 
 
-def test_batched_workload_every_chain(dev):
-    """The batched workload at full size (B=4, T=8192, nk=16, nv=32, carried
-    state; the launch the bench times): every (sequence, head) chain's
-    outputs, final state and all 128 entry states against the oracle's chunk
-    form."""
-    p = I.make_workload(3)
+@pytest.mark.parametrize("index", [2, 3])
+def test_workload_every_chain(dev, index):
+    """The single-stream (T=4096, nv=32) and the batched (B=4, T=8192, nv=32,
+    carried state) workloads at full size, in the launch the bench times:
+    every (sequence, head) chain's outputs, final state and entry states
+    against the oracle's chunk form."""
+    p = I.make_workload(index)
     dp = run(dev, p)
     worst = {}
     for i in range(p.nseq):
