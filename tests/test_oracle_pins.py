@@ -355,3 +355,28 @@ def test_ut_transform_reproduces_the_direct_solves():
         assert rel(Tp[h] @ (np.exp(G[:, h])[:, None] * k_c[:, h]), W[h]) < 1e-12
         assert rel((np.eye(64) + L[h]) @ Tp[h], np.diag(beta[:, h])) < 1e-12
         assert np.all(np.triu(Tp[h], 1) == 0)
+
+
+def test_ut_transform_is_the_neumann_series():
+    """L is strictly lower triangular, hence nilpotent (L^n = 0 for n rows), so
+    (I+L)^-1 is exactly the finite Neumann sum I - L + L^2 - ... + (-L)^(n-1):
+    T' = (sum_j (-L)^j) diag(beta), formed by matrix powers, a different
+    algorithm from the inverse; and for two tokens, by hand,
+    T' = [[b0, 0], [-L10 b0, b1]]."""
+    rng = np.random.default_rng(41)
+    q, k, v, g, beta, h0 = rand_problem(rng, 64, 1, 2, 128, 128)
+    k_c = k[:, kv_head_map(1, 2)]
+    G = chunked_mod.chunk_cumsum(g)
+    L = chunked_mod.gram_strict_lower(k_c, beta, G)
+    Tp = chunked_mod.ut_transform(L, beta)
+    for h in range(2):
+        term = np.eye(64)
+        series = np.eye(64)
+        for _ in range(63):
+            term = -term @ L[h]
+            series = series + term
+        assert np.all(term @ L[h] == 0)  # L^64 = 0
+        assert rel(Tp[h], series * beta[:, h][None, :]) < 1e-12
+    L2 = np.array([[[0.0, 0.0], [0.375, 0.0]]])
+    b2 = np.array([[0.5], [0.25]])
+    assert np.array_equal(chunked_mod.ut_transform(L2, b2)[0], np.array([[0.5, 0.0], [-0.1875, 0.25]]))
