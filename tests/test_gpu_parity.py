@@ -454,6 +454,34 @@ def test_decode_beta_zero_only_decays(dev):
     assert np.abs(out - o_ref).max() <= 2e-2
 
 
+def test_decode_bench_batch_in_full(dev):
+    """The decode the bench times (256 sequences, nk=16, nv=32, carried state,
+    the same token applied step after step): every sequence and head after
+    one step and after a second, against the oracle recurrence run over the
+    token once and twice."""
+    from oracle import gdn_recurrence
+    from parity import seq_arrays
+    p = I.make_problem([1] * 256, nk=16, nv=32, seed=6)
+    print("[gpu] decode B=256 nk=16 nv=32, two steps", flush=True)
+    dp = dev(p, ragged=False)
+    twice = I.Problem([2] * 256, p.nk, p.nv, np.repeat(p.q, 2, axis=0), np.repeat(p.k, 2, axis=0),
+                      np.repeat(p.v, 2, axis=0), np.repeat(p.g, 2, axis=0), np.repeat(p.beta, 2, axis=0),
+                      p.h0, p.seed)
+    cu1, cu2 = p.cu_seqlens, twice.cu_seqlens
+    for step, (prob, cu) in enumerate(((p, cu1), (twice, cu2)), start=1):
+        dp.decode_step(0)
+        torch.cuda.synchronize()
+        out = dp.dec_out.float().cpu().numpy()
+        st = dp.state()
+        o_err = s_err = 0.0
+        for i in range(256):
+            o_ref, h_ref, _ = gdn_recurrence(**seq_arrays(prob, i, cu=cu))
+            o_err = max(o_err, float(np.abs(out[i] - o_ref[-1]).max()))
+            s_err = max(s_err, max(relfro(st[i, h].astype(np.float64), h_ref[h]) for h in range(p.nv)))
+        print(f"decode step {step}: o_maxabs={o_err:.3g} state_relfro={s_err:.3g}", flush=True)
+        assert o_err <= 2e-2 and s_err <= 1e-5
+
+
 def test_prefill_then_decode_continues_the_sequence(dev):
     """Prefill of 130 tokens (ragged chunk tail) leaves the state in place;
     decoding token 131 from it matches the oracle over all 131 tokens."""
