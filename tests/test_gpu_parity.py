@@ -373,6 +373,19 @@ def test_workload_every_chain(dev, index):
     assert_within(worst)
 
 
+def test_ragged_workload_short_sequences_in_full(dev):
+    """The ragged workload (8 sequences, state table) in the bench's launch:
+    every head of each sequence shorter than 5000 tokens (6 of the 8; the two
+    longest are sampled above) against the oracle's chunk form."""
+    p = I.make_workload(4)
+    dp = run(dev, p, state="table", ragged=True)
+    short = [i for i in range(p.nseq) if p.lengths[i] < 5000]
+    assert len(short) >= 4
+    w = check_problem(dp, p, seqs=short, chunked=True)
+    print(f"{len(short)} sequences x {p.nv} heads: {w}", flush=True)
+    assert_within(w)
+
+
 def test_slow_decay_long_carry(dev):
     """g * 0.01 keeps the state alive across many chunks, so a state that is
     not carried (or carried wrongly) between chunks shows in every output."""
