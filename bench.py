@@ -314,7 +314,7 @@ def main():
               flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (--gpus {args.gpus} "
               f"requested); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
