@@ -8,10 +8,13 @@ from the product package: the two share no code.
 
 Modules
 -------
-``recurrence``  the definition: the gated delta rule token by token
-                (Gated DeltaNet, Yang, Kautz & Hatamizadeh, ICLR 2025, the
+``recurrence``  the definition: the gated delta rule token by token (the
+                method the page "spark_model/layers/ops/ssm_gdn_a3.rs" runs
+                as its GDN prefill, kernels gated_delta_rule_chunk_*; the
                 recurrence for S_t and o_t), entry states recorded at every
                 64-token chunk boundary.
+``normalize``   the per-token L2 normalisation of queries and keys that
+                the method applies before the recurrence (``l2_normalize``).
 ``chunked``     the same result reached in 64-token chunks, in the three
                 stages the page "spark_model/layers/ops/ssm_gdn_a3.rs"
                 lists in the doc comment of ``gdn_prefill_fla`` (cumulative
@@ -31,6 +34,7 @@ Conventions shared with the GPU library only through documentation:
 """
 
 from .recurrence import gdn_recurrence, kv_head_map  # noqa: F401
+from .normalize import l2_normalize  # noqa: F401
 from .chunked import (  # noqa: F401
     chunk_cumsum,
     gram_strict_lower,
