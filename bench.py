@@ -2,11 +2,13 @@
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--workload 3]
 
-One step = one gdn_prefill call (both kernels: stage 1, then the spine with the
-output fused in) over the whole synthetic workload, inputs resident in HBM.
+One step = one gdn_prefill_ex call (both kernels: stage 1, then the spine with
+the output fused in) over the whole synthetic workload, inputs resident in HBM.
 Default workload: B=4 sequences of T=8192 tokens, nk=16 k-heads, nv=32
 v-heads, dk=dv=128, carried float32 state updated in place, per-chunk entry
-states emitted.  Prints one JSON line.
+states emitted (the one workload that asks for them; the others run without).
+--raw-qk draws q and k unnormalised and has the kernels normalise them.
+Prints one JSON line.
 
 Warm-up: the W untimed warm-up steps run first; if they took less than 50 ms
 of GPU time, untimed steps continue until 50 ms have passed.  An idle MI355X
@@ -15,9 +17,13 @@ slower than the steady state while clocks settle; the timed K steps are then
 all at steady state.  The line reports the warm-up actually run
 ("warmup_steps_run", "warmup_ms").
 
-roofline: the dominant kernel's algorithmic bytes per launch (the byte model
-below, per token-head / per slot, times the units one launch processes) over
-its average launch time, timed live with HIP events on the launch stream.
+roofline: the dominant kernel's irreducible bytes per launch -- what the
+method must move at least, whatever the implementation: q and k once per
+k-head, v, the output, the entry states where the workload asks for them, and
+the state read and written -- over its average launch time, timed live with
+HIP events on the launch stream; "whole_step" gives the same for the whole
+step (g and beta added).  The implementation's own byte model (its
+intermediates included) is reported beside it as "impl_*".
 traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, read
 from profiles/traffic_<kernel>_<workload>.json when that file was taken on the
 current kernel source (its sha256 matches), else null.
@@ -47,13 +53,39 @@ KERNEL_SRC = {1: "k1_chunk_cumsum_recompute_wu.hip", 2: "k2_chunk_delta_h_fwd_o.
 # byte and flop model (algorithmic: every byte each stage must move once)
 
 
-def algorithmic(p):
-    """Per-kernel algorithmic bytes and flops for problem p (inputs.Problem).
+OPT_ENTRY_STATES, OPT_L2NORM_QK = 0x1, 0x2  # include/gdn_prefill.h
 
-    Bytes: every operand each kernel must read or write once (q, k counted once
-    per k-head).  Stage 1 reads k, g, beta and writes gc, the decays and T'
-    (5 KB per chunk-head); stage 2 reads q, k, v, gc, the decays, T' and the
-    state, and writes the entry states (32 KB per chunk-head), o and the state.
+
+def irreducible(p, entry):
+    """The bytes the method must move at least, for problem p: per kernel
+    (the spine moves q, k, v, the output, the entry states and the state;
+    stage 1 the gates g, beta) and for the whole step.  q and k are counted
+    once per k-head; the entry states only where the workload asks for them
+    (32 KB per chunk-head); the float32 state is read and written once per
+    (sequence, v-head)."""
+    N, nk, nv = p.n_tokens, p.nk, p.nv
+    slots = int(p.cu_chunks[-1]) * nv
+    d = 128
+    qk = 2 * N * nk * d * 2
+    v = N * nv * d * 2
+    o = N * nv * d * 2
+    gb = N * nv * 8
+    s_out = slots * d * d * 2 if entry else 0
+    state = 2 * p.nseq * nv * d * d * 4
+    per = {1: gb, 2: qk + v + o + s_out + state}
+    return per, sum(per.values())
+
+
+def algorithmic(p, flags=OPT_ENTRY_STATES):
+    """Per-kernel bytes and flops of this implementation for problem p
+    (inputs.Problem) and call options.
+
+    Bytes: every operand each kernel reads or writes once (q, k counted once
+    per k-head).  Stage 1 reads k, g, beta (and q with normalisation) and
+    writes gc and T' (10 KB per chunk-head, a bf16 hi + lo pair; with
+    normalisation the row scales, 512 B); stage 2 reads q, k, v, gc, T' (and
+    the row scales) and the state, and writes o, the state and (when asked
+    for) the entry states (32 KB per chunk-head).
     Flops: the dense-tile MFMA work per chunk-head of what each kernel computes
     (Gram in stage 1; K h, T' R, K^T uc, Q h, the scores Q K^T and A uc in
     stage 2), each product counted once."""
@@ -61,23 +93,32 @@ def algorithmic(p):
     slots = int(p.cu_chunks[-1]) * nv
     nseq = p.nseq
     d, C = 128, 64
+    norm = bool(flags & OPT_L2NORM_QK)
     k_bytes = N * nk * d * 2
     q_bytes = N * nk * d * 2
     v_bytes = N * nv * d * 2
     gb_bytes = N * nv * 8
     gc_bytes = slots * C * 4
-    dec_bytes = slots * 2 * C * 4
-    tp_bytes = slots * 2560 * 2  # 2560 float16
-    s_bytes = slots * d * d * 2
+    tp_bytes = slots * 2 * 2560 * 2  # hi + lo, 2560 bf16 each
+    nrm_bytes = slots * 2 * C * 4 if norm else 0
+    s_bytes = slots * d * d * 2 if flags & OPT_ENTRY_STATES else 0
     state_bytes = nseq * nv * d * d * 4
     o_bytes = N * nv * d * 2
     by = {
-        1: k_bytes + gb_bytes + gc_bytes + dec_bytes + tp_bytes,
-        2: q_bytes + k_bytes + v_bytes + gc_bytes + dec_bytes + tp_bytes + 2 * state_bytes + s_bytes + o_bytes,
+        1: k_bytes + (q_bytes if norm else 0) + gb_bytes + gc_bytes + tp_bytes + nrm_bytes,
+        2: q_bytes + k_bytes + v_bytes + gc_bytes + tp_bytes + nrm_bytes + 2 * state_bytes + s_bytes + o_bytes,
     }
     fl = {1: slots * (2 * C * C * d),
           2: slots * (6 * C * d * d + 6 * C * C * d)}
     return by, fl
+
+
+def workload_flags(meta, raw_qk=False, entry_states="auto"):
+    """Call options for a workload: entry states where it asks for them (or as
+    ``entry_states`` = "on" / "off" forces), q/k normalisation in the kernels
+    for raw q, k."""
+    entry = bool(meta.get("entry_states")) if entry_states == "auto" else entry_states == "on"
+    return (OPT_ENTRY_STATES if entry else 0) | (OPT_L2NORM_QK if raw_qk else 0)
 
 
 def source_sha(stage):
@@ -112,10 +153,11 @@ def traffic_for(stage, workload_name):
 def _oracle_worker(args):
     w, workers, seconds = args
     from threadpoolctl import threadpool_limits
-    from oracle import gdn_recurrence, kv_head_map
+    from oracle import gdn_recurrence, kv_head_map, l2_normalize
     from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64
     p = _SAMPLE_PROBLEM
     kmap = kv_head_map(p.nk, p.nv)
+    norm = p.meta.get("raw_qk", False)
     done = 0
     t0 = time.perf_counter()
     with threadpool_limits(1):
@@ -127,6 +169,8 @@ def _oracle_worker(args):
             kap = kmap[[h]]
             q = bf16_to_f64(p.q[a:a + L][:, kap])
             k = bf16_to_f64(p.k[a:a + L][:, kap])
+            if norm:  # the method's per-token normalisation, as the kernels are asked to do it
+                q, k = l2_normalize(q), l2_normalize(k)
             v = bf16_to_f64(p.v[a:a + L][:, [h]])
             g = p.g[a:a + L][:, [h]].astype("float64")
             b = p.beta[a:a + L][:, [h]].astype("float64")
@@ -162,10 +206,11 @@ def cpu_baseline(p, seconds_per_worker=1.5):
         "value": token_heads / wall / p.nv,
         "unit": "tokens/s",
         "cores": workers,
+        "host_cores": os.cpu_count(),
         "kind": "oracle",
-        "sample": (f"{workers} workers (one BLAS thread each) running (sequence, v-head) chains of this "
-                   f"workload through the float64 token recurrence for {seconds_per_worker}s each: "
-                   f"{token_heads} token-heads, {cpu_s:.1f} core-s, wall {wall:.1f}s; "
+        "sample": (f"{workers} workers (one BLAS thread each; the host reports {os.cpu_count()} cores) running "
+                   f"(sequence, v-head) chains of this workload through the float64 token recurrence for "
+                   f"{seconds_per_worker}s each: {token_heads} token-heads, {cpu_s:.1f} core-s, wall {wall:.1f}s; "
                    f"tokens/s = token-heads/s / nv"),
     }
 
@@ -221,7 +266,8 @@ def bench_decode(args):
             res = pool.map(_oracle_decode_worker, [(w, workers, 1.5) for w in range(workers)])
         wall = time.perf_counter() - t0
         heads = sum(r[0] for r in res)
-        cpu = {"value": heads / wall / p.nv, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+        cpu = {"value": heads / wall / p.nv, "unit": "tokens/s", "cores": workers, "host_cores": os.cpu_count(),
+               "kind": "oracle",
                "sample": (f"{workers} workers (one BLAS thread each) running single-token steps of this batch's "
                           f"(sequence, v-head) pairs through the float64 recurrence for 1.5 s each: {heads} "
                           f"head-steps, wall {wall:.1f}s; tokens/s = head-steps/s / nv")}
@@ -276,6 +322,89 @@ def traffic_for_decode():
 
 
 # ---------------------------------------------------------------------------
+# section stamps: cycles per section of the spine's step, from the profiling
+# build (libgdn_prefill_stamps.so, built with -DGDN_SECTION_STAMPS)
+
+STAMP_FIRST, STAMP_STEPS, STAMP_SLOTS, STAMP_WAVES = 8, 32, 16, 8  # gdn_params.h
+COMPUTE_SECTIONS = {  # mark k closes the section that began at mark k-1 (k2_chunk_delta_h_fwd_o.hip)
+    1: "split h (first pair), entry-state tile write, previous chunk's A uc and output tile",
+    2: "Q h (output state term) with the rest of the split",
+    3: "K h rows 0..31 (entry states 0..63 out)",
+    4: "K h rows 32..63, R rows 0..31 (entry states 64..127 out)",
+    5: "T' R rows 0..31 and R rows 32..63",
+    6: "T' R rows 32..63; uc rows 0..31 decayed and split",
+    7: "K^T uc rows 0..31; uc rows 32..63 decayed and split",
+    8: "K^T uc rows 32..63",
+    9: "barrier wait",
+}
+LOADER_SECTIONS = {1: "stage chunk c+1 into LDS (active pair)", 2: "issue fetch of chunk c+3 (active pair)",
+                   3: "scores / output stores (idle pair)", 4: "barrier wait"}
+
+
+def section_stamps(args):
+    """Run the workload with the profiling build, stamp one step window of
+    workgroup 0 (sequence 0, v-head 0), and print cycles per section."""
+    import numpy as np
+    import torch
+    from linear_attention_ssm_chunk_amd import binding, build
+    L = binding.load(build.LIB_STAMPS)
+    import ctypes
+    L.gdn_debug_set_stamps.argtypes = [ctypes.c_void_p]
+    from linear_attention_ssm_chunk_amd import inputs as I
+    from linear_attention_ssm_chunk_amd.device import DeviceProblem
+    p = I.make_workload(args.workload, raw_qk=args.raw_qk)
+    flags = workload_flags(p.meta, args.raw_qk, args.entry_states)
+    kw = dict(flags=flags)
+    if p.meta["layout"] == "conv":
+        kw["layout"] = "conv"
+    elif p.meta["layout"] == "varlen_table":
+        kw.update(state="table", ragged=True)
+    dp = DeviceProblem(p, **kw)
+    t0 = time.perf_counter()
+    n = 0
+    while n < args.warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
+        dp.run()
+        n += 1
+        torch.cuda.synchronize()
+    buf = torch.zeros(STAMP_WAVES * STAMP_STEPS * STAMP_SLOTS, dtype=torch.int64, device="cuda")
+    L.gdn_debug_set_stamps(buf.data_ptr())
+    dp.run()
+    torch.cuda.synchronize()
+    L.gdn_debug_set_stamps(None)
+    st = buf.cpu().numpy().astype(np.int64).reshape(STAMP_WAVES, STAMP_STEPS, STAMP_SLOTS)
+    chains = p.nseq * p.nv
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    strips = 1 if chains * 8 <= cus else 2 if chains * 4 <= cus else 4
+    nch = int(p.cu_chunks[1] - p.cu_chunks[0])
+    steps = min(STAMP_STEPS, nch - STAMP_FIRST) - 1  # full steps in the window
+    w0 = st[0]
+    step_cyc = np.diff(w0[:steps + 1, 0])
+    step_rt = np.diff(w0[:steps + 1, 15])  # 100 MHz ticks
+    clock = float(step_cyc.sum() / step_rt.sum() * 0.1)  # GHz
+    comp = {COMPUTE_SECTIONS[k]: round(float(np.mean(w0[:steps, k] - w0[:steps, k - 1])), 1) for k in range(1, 10)}
+    loaders = {}
+    for w in range(strips, strips + 4):
+        li = w - strips
+        role = (1 - (li >> 1)) if strips <= 2 else (li >> 1)
+        pair = li & 1
+        t = st[w].astype(np.float64)
+        # a loader stages in step c when (c + 1) % 2 == pair and is idle otherwise
+        act = [c for c in range(steps) if (STAMP_FIRST + c + 1) % 2 == pair]
+        idle = [c for c in range(steps) if (STAMP_FIRST + c) % 2 == pair]
+        mean = lambda cs, k1, k0: round(float(np.mean([t[c, k1] - t[c, k0] for c in cs])), 1)  # noqa: E731
+        loaders[f"wave {w} (role {role})"] = {
+            "active step: " + LOADER_SECTIONS[1]: mean(act, 1, 0),
+            "active step: " + LOADER_SECTIONS[2]: mean(act, 2, 1),
+            "active step: " + LOADER_SECTIONS[4]: mean(act, 4, 3),
+            "idle step: " + LOADER_SECTIONS[3]: mean(idle, 3, 0),
+            "idle step: " + LOADER_SECTIONS[4]: mean(idle, 4, 3)}
+    out = {"workload": p.meta["name"], "entry_states": bool(flags & OPT_ENTRY_STATES),
+           "strips_per_workgroup": strips, "chunks": nch,
+           "stamped_steps": f"{STAMP_FIRST}..{STAMP_FIRST + steps - 1} of sequence 0, v-head 0, workgroup 0",
+           "clock_GHz": round(clock, 3), "cycles_per_step": round(float(step_cyc.mean()), 1),
+           "us_per_step": round(float(step_rt.mean()) / 100.0, 3),
+           "compute_wave_0": comp, "loaders": loaders}
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -285,8 +414,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entry-states", choices=("auto", "on", "off"), default="auto",
+                    help="emit the per-chunk entry states: auto = where the workload asks for them")
+    ap.add_argument("--raw-qk", action="store_true",
+                    help="draw q and k unnormalised and have the kernels normalise them (GDN_OPT_L2NORM_QK)")
     ap.add_argument("--decode", action="store_true",
                     help="measure the recurrent decode step (gdn_decode) on a batch of 256 sequences instead")
+    ap.add_argument("--section-stamps", action="store_true",
+                    help="cycles per section of the spine's step from the profiling build (not a timing run)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (three times), to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -321,20 +456,26 @@ def main():
     if args.decode:
         bench_decode(args)
         return
+    if args.section_stamps:
+        section_stamps(args)
+        return
 
     from linear_attention_ssm_chunk_amd import inputs as I
-    p = I.make_workload(args.workload)
-    wname = p.meta["name"]
+    p = I.make_workload(args.workload, raw_qk=args.raw_qk)
+    wname = p.meta["name"] + ("_raw_qk" if args.raw_qk else "")
+    flags = workload_flags(p.meta, args.raw_qk, args.entry_states)
+    if args.entry_states != "auto":
+        wname += f"_entry_{args.entry_states}"
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(p)
 
     import torch
     from linear_attention_ssm_chunk_amd.device import DeviceProblem
-    kw = {}
+    kw = dict(flags=flags)
     if p.meta["layout"] == "conv":
-        kw = dict(layout="conv")
+        kw["layout"] = "conv"
     elif p.meta["layout"] == "varlen_table":
-        kw = dict(state="table", ragged=True)
+        kw.update(state="table", ragged=True)
     dp = DeviceProblem(p, **kw)
 
     # warm-up: W steps, then more untimed steps until 50 ms of GPU time have run
@@ -368,12 +509,17 @@ def main():
     tokens = p.n_tokens
     value = tokens / (ms_per_step / 1e3)
 
-    by, fl = algorithmic(p)
+    entry = bool(flags & OPT_ENTRY_STATES)
+    io, io_total = irreducible(p, entry)
+    by, fl = algorithmic(p, flags)
     dom = max(per, key=per.get)
-    achieved = by[dom] / (per[dom] / 1e3) / 1e9
-    kernels = {KERNELS[st]: {"ms": round(per[st], 4), "alg_bytes": by[st],
-                             "alg_GBps": round(by[st] / (per[st] / 1e3) / 1e9, 1),
-                             "hbm_frac": round(by[st] / (per[st] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+    gbps = lambda b, ms: b / (ms / 1e3) / 1e9  # noqa: E731
+    achieved = gbps(io[dom], per[dom])
+    kernels = {KERNELS[st]: {"ms": round(per[st], 4), "io_bytes": io[st],
+                             "io_GBps": round(gbps(io[st], per[st]), 1),
+                             "io_frac": round(gbps(io[st], per[st]) / HBM_PEAK_GBS, 4),
+                             "impl_bytes": by[st], "impl_GBps": round(gbps(by[st], per[st]), 1),
+                             "impl_frac": round(gbps(by[st], per[st]) / HBM_PEAK_GBS, 4),
                              "mfma_frac": round(fl[st] / (per[st] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
                for st in stages}
     total_bytes = sum(by.values())
@@ -394,13 +540,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": wname, "B": p.nseq, "T": max(p.lengths), "n_tokens": tokens, "nk": p.nk,
                    "nv": p.nv, "dk": 128, "dv": 128, "chunk": 64, "global_batch": p.nseq,
-                   "seq_len": max(p.lengths), "parallelism": "single_gpu"},
+                   "seq_len": max(p.lengths), "parallelism": "single_gpu", "entry_states": entry,
+                   "qk_normalised_in_kernels": bool(flags & OPT_L2NORM_QK)},
         "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(dom, wname)},
+                     "traffic": traffic_for(dom, wname), "bytes_per_launch": io[dom],
+                     "bytes": "irreducible: q and k once per k-head, v, o, entry states where asked for, "
+                              "state in and out",
+                     "impl_bytes_per_launch": by[dom],
+                     "impl_frac": round(gbps(by[dom], per[dom]) / HBM_PEAK_GBS, 4)},
         "kernels": kernels,
-        "whole_step": {"alg_bytes": total_bytes,
-                       "alg_GBps": round(total_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "whole_step": {"io_bytes": io_total, "io_GBps": round(gbps(io_total, ms_per_step), 1),
+                       "io_frac": round(gbps(io_total, ms_per_step) / HBM_PEAK_GBS, 4),
+                       "impl_bytes": total_bytes, "impl_GBps": round(gbps(total_bytes, ms_per_step), 1),
                        "mfma_frac": round(sum(fl.values()) / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,
     }

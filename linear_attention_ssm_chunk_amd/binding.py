@@ -21,6 +21,9 @@ GDN_ESCRATCH = -3
 GDN_EHIP = -4
 GDN_CHUNK = 64
 GDN_HEAD_DIM = 128
+GDN_OPT_ENTRY_STATES = 0x1
+GDN_OPT_L2NORM_QK = 0x2
+GDN_NO_REGION = ctypes.c_size_t(-1).value
 
 
 class gdn_strides(ctypes.Structure):
@@ -33,9 +36,9 @@ class gdn_varlen(ctypes.Structure):
 
 
 class gdn_scratch_layout(ctypes.Structure):
-    _fields_ = [("gc", ctypes.c_size_t), ("dec", ctypes.c_size_t), ("tp", ctypes.c_size_t),
+    _fields_ = [("gc", ctypes.c_size_t), ("tp", ctypes.c_size_t), ("nrm", ctypes.c_size_t),
                 ("s_entry", ctypes.c_size_t), ("total", ctypes.c_size_t),
-                ("slots", ctypes.c_int64)]
+                ("slots", ctypes.c_int64), ("flags", ctypes.c_uint)]
 
 
 class GdnError(RuntimeError):
@@ -47,39 +50,61 @@ class GdnError(RuntimeError):
 _lib = None
 
 
-def lib():
-    """The loaded library (loaded on first use)."""
+def load(path=None):
+    """Load the library from ``path`` (default LIB_PATH; bench.py's section-stamp
+    profiling loads libgdn_prefill_stamps.so this way before anything else).
+    Once a library is loaded, every call goes to it."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run python -m linear_attention_ssm_chunk_amd.build")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-        common = [vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, i32, i32, i32, i32, i32, i32,
-                  ctypes.POINTER(gdn_strides), ctypes.POINTER(gdn_varlen)]
-        L.gdn_prefill.argtypes = common + [vp]
-        L.gdn_prefill.restype = i32
-        L.gdn_prefill_stage.argtypes = [i32] + common + [vp]
-        L.gdn_prefill_stage.restype = i32
-        L.gdn_prefill_validate.argtypes = common
-        L.gdn_prefill_validate.restype = i32
-        L.gdn_prefill_scratch_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen)]
-        L.gdn_prefill_scratch_bytes.restype = sz
-        L.gdn_prefill_scratch_layout.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen),
-                                                 ctypes.POINTER(gdn_scratch_layout)]
-        L.gdn_prefill_scratch_layout.restype = i32
-        L.gdn_varlen_check_host.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
-                                            ctypes.c_int32, ctypes.c_int32]
-        L.gdn_varlen_check_host.restype = i32
-        dec = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_strides)]
-        L.gdn_decode.argtypes = dec + [vp]
-        L.gdn_decode.restype = i32
-        L.gdn_decode_validate.argtypes = dec
-        L.gdn_decode_validate.restype = i32
-        L.gdn_last_error.argtypes = []
-        L.gdn_last_error.restype = ctypes.c_char_p
-        _lib = L
+        path = LIB_PATH if path is None else path
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run python -m linear_attention_ssm_chunk_amd.build")
+        _lib = _declare(ctypes.CDLL(path))
     return _lib
+
+
+def lib():
+    """The loaded library (loaded on first use)."""
+    return load()
+
+
+def _declare(L):
+    """Argument and result types of every exported function."""
+    vp, i32, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint
+    common = [vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, i32, i32, i32, i32, i32, i32,
+              ctypes.POINTER(gdn_strides), ctypes.POINTER(gdn_varlen)]
+    L.gdn_prefill.argtypes = common + [vp]
+    L.gdn_prefill.restype = i32
+    L.gdn_prefill_ex.argtypes = common + [u32, vp]
+    L.gdn_prefill_ex.restype = i32
+    L.gdn_prefill_stage.argtypes = [i32] + common + [vp]
+    L.gdn_prefill_stage.restype = i32
+    L.gdn_prefill_stage_ex.argtypes = [i32] + common + [u32, vp]
+    L.gdn_prefill_stage_ex.restype = i32
+    L.gdn_prefill_validate.argtypes = common
+    L.gdn_prefill_validate.restype = i32
+    L.gdn_prefill_validate_ex.argtypes = common + [u32]
+    L.gdn_prefill_validate_ex.restype = i32
+    dims = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_varlen)]
+    L.gdn_prefill_scratch_bytes.argtypes = dims
+    L.gdn_prefill_scratch_bytes.restype = sz
+    L.gdn_prefill_scratch_bytes_ex.argtypes = dims + [u32]
+    L.gdn_prefill_scratch_bytes_ex.restype = sz
+    L.gdn_prefill_scratch_layout.argtypes = dims + [ctypes.POINTER(gdn_scratch_layout)]
+    L.gdn_prefill_scratch_layout.restype = i32
+    L.gdn_prefill_scratch_layout_ex.argtypes = dims + [u32, ctypes.POINTER(gdn_scratch_layout)]
+    L.gdn_prefill_scratch_layout_ex.restype = i32
+    L.gdn_varlen_check_host.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.c_int32, ctypes.c_int32]
+    L.gdn_varlen_check_host.restype = i32
+    dec = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_strides)]
+    L.gdn_decode.argtypes = dec + [vp]
+    L.gdn_decode.restype = i32
+    L.gdn_decode_validate.argtypes = dec
+    L.gdn_decode_validate.restype = i32
+    L.gdn_last_error.argtypes = []
+    L.gdn_last_error.restype = ctypes.c_char_p
+    return L
 
 
 def _ptr(x):
@@ -135,11 +160,32 @@ def gdn_prefill(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scrat
     return rc
 
 
+def gdn_prefill_ex(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                   B, T, nk, nv, dk, dv, strides, varlen, flags, stream):
+    """gdn_prefill with GDN_OPT_* flags.  Raises GdnError on a nonzero return."""
+    args, keep = _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen)
+    rc = lib().gdn_prefill_ex(*args, int(flags), ctypes.c_void_p(int(stream)))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return rc
+
+
 def gdn_prefill_stage(stage, q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
                       B, T, nk, nv, dk, dv, strides, varlen, stream):
     args, keep = _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
                          B, T, nk, nv, dk, dv, strides, varlen)
     rc = lib().gdn_prefill_stage(int(stage), *args, ctypes.c_void_p(int(stream)))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return rc
+
+
+def gdn_prefill_stage_ex(stage, q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen, flags, stream):
+    args, keep = _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen)
+    rc = lib().gdn_prefill_stage_ex(int(stage), *args, int(flags), ctypes.c_void_p(int(stream)))
     if rc != GDN_OK:
         raise GdnError(rc, gdn_last_error())
     return rc
@@ -153,9 +199,21 @@ def gdn_prefill_validate(q, k, v, g, beta, h_state, h_state_is_table, out, scrat
     return lib().gdn_prefill_validate(*args)
 
 
+def gdn_prefill_validate_ex(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                            B, T, nk, nv, dk, dv, strides, varlen, flags):
+    args, keep = _common(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes,
+                         B, T, nk, nv, dk, dv, strides, varlen)
+    return lib().gdn_prefill_validate_ex(*args, int(flags))
+
+
 def gdn_prefill_scratch_bytes(B, T, nk, nv, dk, dv, varlen=None):
     vl = _varlen(varlen)
     return lib().gdn_prefill_scratch_bytes(B, T, nk, nv, dk, dv, _ref(vl))
+
+
+def gdn_prefill_scratch_bytes_ex(B, T, nk, nv, dk, dv, varlen=None, flags=GDN_OPT_ENTRY_STATES):
+    vl = _varlen(varlen)
+    return lib().gdn_prefill_scratch_bytes_ex(B, T, nk, nv, dk, dv, _ref(vl), int(flags))
 
 
 def gdn_prefill_scratch_layout(B, T, nk, nv, dk, dv, varlen=None):
@@ -167,13 +225,23 @@ def gdn_prefill_scratch_layout(B, T, nk, nv, dk, dv, varlen=None):
     return out
 
 
-def gdn_varlen_check_host(B, cu_seqlens, cu_chunks, max_chunks, total_chunks):
-    """Check host copies of the ragged offsets (sequences of ints)."""
+def gdn_prefill_scratch_layout_ex(B, T, nk, nv, dk, dv, varlen=None, flags=GDN_OPT_ENTRY_STATES):
+    vl = _varlen(varlen)
+    out = gdn_scratch_layout()
+    rc = lib().gdn_prefill_scratch_layout_ex(B, T, nk, nv, dk, dv, _ref(vl), int(flags), ctypes.byref(out))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return out
+
+
+def gdn_varlen_check_host(B, T, cu_seqlens, cu_chunks, max_chunks, total_chunks):
+    """Check host copies of the ragged offsets (sequences of ints) for a call
+    with T tokens in all."""
     if len(cu_seqlens) < B + 1 or len(cu_chunks) < B + 1:
         raise ValueError(f"offsets: {len(cu_seqlens)} and {len(cu_chunks)} entries given, B + 1 = {B + 1} needed")
     a = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
     b = (ctypes.c_int32 * len(cu_chunks))(*[int(x) for x in cu_chunks])
-    return lib().gdn_varlen_check_host(B, a, b, int(max_chunks), int(total_chunks))
+    return lib().gdn_varlen_check_host(B, int(T), a, b, int(max_chunks), int(total_chunks))
 
 
 def _decode_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides):

@@ -1,6 +1,11 @@
 """Build libgdn_prefill.so in-tree with hipcc for gfx950.
 
-    python -m linear_attention_ssm_chunk_amd.build
+    python -m linear_attention_ssm_chunk_amd.build            # the library
+    python -m linear_attention_ssm_chunk_amd.build --stamps   # and its section-stamp profiling build
+
+The profiling build (libgdn_prefill_stamps.so, -DGDN_SECTION_STAMPS) is the same
+sources with clock stamps at the spine's section marks; bench.py
+--section-stamps loads it.  Nothing else loads it.
 
 Every HIP source is compiled with packed FP32 math disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns
@@ -17,6 +22,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn_prefill.so")
+LIB_STAMPS = os.path.join(PKG, "libgdn_prefill_stamps.so")
 SOURCES = ["gdn_api.hip", "k1_chunk_cumsum_recompute_wu.hip", "k2_chunk_delta_h_fwd_o.hip",
            "k3_recurrent_decode.hip"]
 ARCH = "gfx950"
@@ -33,11 +39,13 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False):
-    """Compile every kernel and the C ABI into one shared library."""
+def build(verbose=False, stamps=False):
+    """Compile every kernel and the C ABI into one shared library (with
+    ``stamps``: the section-stamp profiling build)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + srcs + ["-o", tmp]
+    lib = LIB_STAMPS if stamps else LIB
+    tmp = lib + ".tmp"
+    cmd = [hipcc()] + FLAGS + (["-DGDN_SECTION_STAMPS"] if stamps else []) + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,9 +55,11 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--stamps" in sys.argv[1:]:
+        print(build(verbose=True, stamps=True))

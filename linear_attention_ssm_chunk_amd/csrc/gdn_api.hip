@@ -76,34 +76,56 @@ int64_t chunk_slots(int B, int T, const gdn_varlen *varlen) {
   return int64_t(B) * ((int64_t(T) + GDN_CHUNK - 1) / GDN_CHUNK);
 }
 
-int layout(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen, gdn_scratch_layout *out) {
+int check_flags(unsigned flags) {
+  if (flags & ~unsigned(GDN_OPT_ENTRY_STATES | GDN_OPT_L2NORM_QK))
+    return fail(GDN_EINVAL, "flags=0x%x: only GDN_OPT_ENTRY_STATES (0x%x) and GDN_OPT_L2NORM_QK (0x%x) exist", flags,
+                unsigned(GDN_OPT_ENTRY_STATES), unsigned(GDN_OPT_L2NORM_QK));
+  return GDN_OK;
+}
+
+// The regions gc, tp, [nrm], [s_entry] of `slots` chunk slots, from byte 0,
+// each 256-byte aligned; absent regions get GDN_NO_REGION.
+void place_regions(int64_t slots, unsigned flags, gdn_scratch_layout *out) {
+  size_t off = 0;
+  out->slots = slots;
+  out->flags = flags;
+  out->gc = off;
+  off = align256(off + size_t(slots) * gdn::kGcBytes);
+  out->tp = off;
+  off = align256(off + size_t(slots) * gdn::kTpBytes);
+  out->nrm = GDN_NO_REGION;
+  if (flags & GDN_OPT_L2NORM_QK) {
+    out->nrm = off;
+    off = align256(off + size_t(slots) * gdn::kNrmBytes);
+  }
+  out->s_entry = GDN_NO_REGION;
+  if (flags & GDN_OPT_ENTRY_STATES) {
+    out->s_entry = off;
+    off = align256(off + size_t(slots) * gdn::kSBytes);
+  }
+  out->total = off > 256 ? off : 256; // never 0 for a valid problem
+}
+
+int layout(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen, unsigned flags,
+           gdn_scratch_layout *out) {
   if (dk != GDN_HEAD_DIM || dv != GDN_HEAD_DIM)
     return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
   if (nv <= 0 || nk <= 0 || nv % nk != 0)
     return fail(GDN_EINVAL, "head counts: nk=%d nv=%d (nv must be a positive multiple of nk)", nk, nv);
+  int rc = check_flags(flags);
+  if (rc != GDN_OK) return rc;
   const int64_t chunks = chunk_slots(B, T, varlen);
   if (chunks < 0)
     return fail(GDN_EINVAL, "sizes: B=%d T=%d%s give no valid chunk count", B, T,
                 varlen ? " (ragged: max_chunks/total_chunks must be >= 0)" : "");
-  const int64_t slots = chunks * nv;
-  size_t off = 0;
-  out->slots = slots;
-  out->gc = off;
-  off = align256(off + size_t(slots) * gdn::kGcBytes);
-  out->dec = off;
-  off = align256(off + size_t(slots) * gdn::kDecBytes);
-  out->tp = off;
-  off = align256(off + size_t(slots) * gdn::kTpBytes);
-  out->s_entry = off;
-  off = align256(off + size_t(slots) * gdn::kSBytes);
-  out->total = off > 256 ? off : 256; // never 0 for a valid problem
+  place_regions(chunks * nv, flags, out);
   return ok();
 }
 
-int validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
-             void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
-             int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
-             const gdn_varlen *varlen, gdn_scratch_layout *lay) {
+// Every argument check of gdn_prefill_ex except the scratch buffer's.
+int validate_args(const void *q, const void *k, const void *v, const float *g, const float *beta, void *h_state,
+                  int h_state_is_table, void *out, int B, int T, int nk, int nv, int dk, int dv,
+                  const gdn_strides *strides, const gdn_varlen *varlen, unsigned flags) {
   if (dk != GDN_HEAD_DIM || dv != GDN_HEAD_DIM)
     return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
   if (nk <= 0 || nv <= 0) return fail(GDN_EINVAL, "head counts: nk=%d nv=%d must be positive", nk, nv);
@@ -117,7 +139,6 @@ int validate(const void *q, const void *k, const void *v, const float *g, const 
   if (!no_tokens && (!g || !beta)) return fail(GDN_EINVAL, "null pointer: g and beta are required");
   if (!h_state) return fail(GDN_EINVAL, "null pointer: h_state is required");
   if (!no_tokens && !out) return fail(GDN_EINVAL, "null pointer: out is required");
-  if (!scratch) return fail(GDN_EINVAL, "null pointer: scratch is required");
   if (!strides) return fail(GDN_EINVAL, "null pointer: strides is required");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
     return fail(GDN_EINVAL, "alignment: q, k and v must be 16-byte aligned (16-byte vector loads)");
@@ -125,7 +146,6 @@ int validate(const void *q, const void *k, const void *v, const float *g, const 
   if (!aligned(h_state, h_state_is_table ? 8 : 16))
     return fail(GDN_EINVAL, "alignment: h_state must be 16-byte aligned (8 for a pointer table)");
   if (!aligned(out, 16)) return fail(GDN_EINVAL, "alignment: out must be 16-byte aligned");
-  if (!aligned(scratch, 256)) return fail(GDN_EINVAL, "alignment: scratch must be 256-byte aligned");
   if (h_state_is_table != 0 && h_state_is_table != 1)
     return fail(GDN_EINVAL, "h_state_is_table=%d must be 0 or 1", h_state_is_table);
   if (strides->qk_row % 8 != 0 || strides->v_row % 8 != 0)
@@ -158,20 +178,44 @@ int validate(const void *q, const void *k, const void *v, const float *g, const 
                   varlen->total_chunks);
     if (int64_t(varlen->total_chunks) * GDN_CHUNK < int64_t(T))
       return fail(GDN_EINVAL, "ragged: total_chunks=%d cannot hold T=%d tokens", varlen->total_chunks, T);
+    // every chunk holds at least one token, so the offsets cannot describe
+    // more chunks than tokens (and with T == 0 none at all: the token
+    // pointers may then be NULL only because nothing is launched)
+    if (int64_t(varlen->total_chunks) > int64_t(T))
+      return fail(GDN_EINVAL, "ragged: total_chunks=%d exceeds T=%d tokens (a chunk holds at least one token)",
+                  varlen->total_chunks, T);
   }
-  int rc = check_extents(B, T, nk, nv, varlen);
+  int rc = check_flags(flags);
   if (rc != GDN_OK) return rc;
-  rc = layout(B, T, nk, nv, dk, dv, varlen, lay);
+  return check_extents(B, T, nk, nv, varlen);
+}
+
+int validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
+             void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
+             int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+             const gdn_varlen *varlen, unsigned flags, gdn_scratch_layout *lay) {
+  int rc = validate_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, T, nk, nv, dk, dv, strides, varlen,
+                         flags);
+  if (rc != GDN_OK) return rc;
+  if (!scratch) return fail(GDN_EINVAL, "null pointer: scratch is required");
+  if (!aligned(scratch, 256)) return fail(GDN_EINVAL, "alignment: scratch must be 256-byte aligned");
+  rc = layout(B, T, nk, nv, dk, dv, varlen, flags, lay);
   if (rc != GDN_OK) return rc;
   if (scratch_bytes < lay->total)
     return fail(GDN_ESCRATCH, "scratch: %zu bytes given, %zu needed", scratch_bytes, lay->total);
   return ok();
 }
 
+#ifdef GDN_SECTION_STAMPS
+unsigned long long *g_stamps = nullptr; // profiling build: where the spine's section stamps go
+#endif
+
+// The parameter block.  scratch holds the regions of `lay`; the entry states
+// go to s_entry_out when it is given, else to the scratch's s_entry region.
 gdn::Params make_params(const void *q, const void *k, const void *v, const float *g, const float *beta,
                         void *h_state, int h_state_is_table, void *out, void *scratch, int B, int T,
                         int nk, int nv, const gdn_strides *strides, const gdn_varlen *varlen,
-                        const gdn_scratch_layout &lay) {
+                        const gdn_scratch_layout &lay, void *s_entry_out = nullptr) {
   gdn::Params p{};
   unsigned char *base = static_cast<unsigned char *>(scratch);
   p.q = static_cast<const uint16_t *>(q);
@@ -183,9 +227,16 @@ gdn::Params make_params(const void *q, const void *k, const void *v, const float
   p.h_is_table = h_state_is_table;
   p.out = static_cast<uint16_t *>(out);
   p.gc = reinterpret_cast<float *>(base + lay.gc);
-  p.dec = reinterpret_cast<float *>(base + lay.dec);
   p.tp = reinterpret_cast<uint16_t *>(base + lay.tp);
-  p.s_entry = reinterpret_cast<uint16_t *>(base + lay.s_entry);
+  p.nrm = lay.nrm == GDN_NO_REGION ? nullptr : reinterpret_cast<float *>(base + lay.nrm);
+  if (s_entry_out)
+    p.s_entry = static_cast<uint16_t *>(s_entry_out);
+  else
+    p.s_entry = lay.s_entry == GDN_NO_REGION ? nullptr : reinterpret_cast<uint16_t *>(base + lay.s_entry);
+  p.opts = lay.flags;
+#ifdef GDN_SECTION_STAMPS
+  p.stamps = g_stamps;
+#endif
   p.qk_row = strides->qk_row;
   p.v_row = strides->v_row;
   p.gb_row = strides->gb_row;
@@ -261,48 +312,74 @@ int validate_decode(const void *q, const void *k, const void *v, const float *g,
 
 extern "C" {
 
-size_t gdn_prefill_scratch_bytes(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen) {
+size_t gdn_prefill_scratch_bytes_ex(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen,
+                                    unsigned flags) {
   gdn_scratch_layout lay;
-  if (layout(B, T, nk, nv, dk, dv, varlen, &lay) != GDN_OK) return 0;
+  if (layout(B, T, nk, nv, dk, dv, varlen, flags, &lay) != GDN_OK) return 0;
   return lay.total;
+}
+
+size_t gdn_prefill_scratch_bytes(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen) {
+  return gdn_prefill_scratch_bytes_ex(B, T, nk, nv, dk, dv, varlen, GDN_OPT_ENTRY_STATES);
+}
+
+int gdn_prefill_scratch_layout_ex(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen,
+                                  unsigned flags, gdn_scratch_layout *out) {
+  if (!out) return fail(GDN_EINVAL, "null pointer: layout output is required");
+  return layout(B, T, nk, nv, dk, dv, varlen, flags, out);
 }
 
 int gdn_prefill_scratch_layout(int B, int T, int nk, int nv, int dk, int dv, const gdn_varlen *varlen,
                                gdn_scratch_layout *out) {
-  if (!out) return fail(GDN_EINVAL, "null pointer: layout output is required");
-  return layout(B, T, nk, nv, dk, dv, varlen, out);
+  return gdn_prefill_scratch_layout_ex(B, T, nk, nv, dk, dv, varlen, GDN_OPT_ENTRY_STATES, out);
+}
+
+int gdn_prefill_validate_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
+                            int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+                            const gdn_varlen *varlen, unsigned flags) {
+  gdn_scratch_layout lay;
+  return validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk, nv, dk, dv,
+                  strides, varlen, flags, &lay);
 }
 
 int gdn_prefill_validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
                          void *h_state, int h_state_is_table, void *out, void *scratch,
                          size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
                          const gdn_strides *strides, const gdn_varlen *varlen) {
-  gdn_scratch_layout lay;
-  return validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk, nv,
-                  dk, dv, strides, varlen, &lay);
+  return gdn_prefill_validate_ex(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T,
+                                 nk, nv, dk, dv, strides, varlen, GDN_OPT_ENTRY_STATES);
 }
 
-int gdn_prefill_stage(int stage, const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, void *h_state, int h_state_is_table, void *out, void *scratch,
-                      size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
-                      const gdn_strides *strides, const gdn_varlen *varlen, void *stream) {
+int gdn_prefill_stage_ex(int stage, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, void *h_state, int h_state_is_table, void *out, void *scratch,
+                         size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
+                         const gdn_strides *strides, const gdn_varlen *varlen, unsigned flags, void *stream) {
   if (stage < 1 || stage > 2) return fail(GDN_EINVAL, "stage=%d must be 1 or 2", stage);
   gdn_scratch_layout lay;
   int rc = validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk,
-                    nv, dk, dv, strides, varlen, &lay);
+                    nv, dk, dv, strides, varlen, flags, &lay);
   if (rc != GDN_OK) return rc;
   const gdn::Params p = make_params(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, B, T, nk,
                                     nv, strides, varlen, lay);
   return run_stage(stage, p, static_cast<hipStream_t>(stream));
 }
 
-int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
-                int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
-                const gdn_varlen *varlen, void *stream) {
+int gdn_prefill_stage(int stage, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, void *h_state, int h_state_is_table, void *out, void *scratch,
+                      size_t scratch_bytes, int B, int T, int nk, int nv, int dk, int dv,
+                      const gdn_strides *strides, const gdn_varlen *varlen, void *stream) {
+  return gdn_prefill_stage_ex(stage, q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B,
+                              T, nk, nv, dk, dv, strides, varlen, GDN_OPT_ENTRY_STATES, stream);
+}
+
+int gdn_prefill_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                   void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
+                   int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+                   const gdn_varlen *varlen, unsigned flags, void *stream) {
   gdn_scratch_layout lay;
   int rc = validate(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk,
-                    nv, dk, dv, strides, varlen, &lay);
+                    nv, dk, dv, strides, varlen, flags, &lay);
   if (rc != GDN_OK) return rc;
   const gdn::Params p = make_params(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, B, T, nk,
                                     nv, strides, varlen, lay);
@@ -313,9 +390,18 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
   return GDN_OK;
 }
 
-int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *cu_chunks_host,
+int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                void *h_state, int h_state_is_table, void *out, void *scratch, size_t scratch_bytes,
+                int B, int T, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+                const gdn_varlen *varlen, void *stream) {
+  return gdn_prefill_ex(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk, nv,
+                        dk, dv, strides, varlen, GDN_OPT_ENTRY_STATES, stream);
+}
+
+int gdn_varlen_check_host(int B, int T, const int32_t *cu_seqlens_host, const int32_t *cu_chunks_host,
                           int32_t max_chunks, int32_t total_chunks) {
   if (B <= 0) return fail(GDN_EINVAL, "B=%d must be positive", B);
+  if (T < 0) return fail(GDN_EINVAL, "T=%d (total tokens) must be >= 0", T);
   if (!cu_seqlens_host || !cu_chunks_host) return fail(GDN_EINVAL, "null pointer: offsets are required");
   if (cu_seqlens_host[0] != 0 || cu_chunks_host[0] != 0)
     return fail(GDN_EINVAL, "ragged: cu_seqlens[0] and cu_chunks[0] must be 0");
@@ -329,6 +415,8 @@ int gdn_varlen_check_host(int B, const int32_t *cu_seqlens_host, const int32_t *
                   (long long)len, (long long)nch);
     if (nch > mx) mx = int32_t(nch);
   }
+  if (cu_seqlens_host[B] != T)
+    return fail(GDN_EINVAL, "ragged: cu_seqlens[B]=%d but T=%d tokens", cu_seqlens_host[B], T);
   if (mx != max_chunks)
     return fail(GDN_EINVAL, "ragged: max_chunks=%d but the longest sequence has %d chunks", max_chunks, mx);
   if (cu_chunks_host[B] != total_chunks)
@@ -369,5 +457,12 @@ int gdn_decode(const void *q, const void *k, const void *v, const float *g, cons
 }
 
 const char *gdn_last_error(void) { return g_err; }
+
+#ifdef GDN_SECTION_STAMPS
+// Profiling build only: the device buffer (kStampWaves * kStampSteps *
+// kStampSlots 64-bit words) that the spine's workgroup 0 stamps; NULL stops it.
+// The stamps are written only while a buffer is set.
+void gdn_debug_set_stamps(void *buf) { g_stamps = static_cast<unsigned long long *>(buf); }
+#endif
 
 } // extern "C"

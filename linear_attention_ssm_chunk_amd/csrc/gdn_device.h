@@ -15,9 +15,10 @@
 // tiles an operand of the next product without moving data between lanes:
 // registers (tile 2j, tile 2j+1) of a C result are exactly the k = 32j..32j+31
 // block of a B (or, read as its transpose, an A) operand.
-// A product with an identity operand moves a tile between the two
-// orientations in registers (exact for bf16 data): that is how these kernels
-// transpose, instead of staging through LDS.
+// Where a tile is needed in the other orientation, the kernels read it from
+// LDS with the transposing read ds_read_b64_tr_b16 (K^T and V in the spine, the
+// entry states on their way out), or form the product transposed (the
+// spine's output, O^T = h^T Q^T + uc^T A^T).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -77,7 +78,9 @@ __device__ __forceinline__ bf16x8 load16_bf16x8(const uint16_t *p) {
 }
 
 // Where a sequence lives.  Ragged offsets are checked here so that a bad table
-// skips the sequence instead of writing outside the scratch.
+// skips the sequence instead of reading or writing outside the caller's token
+// rows (cu_seqlens within [0, T]) or the scratch (cu_chunks within
+// [0, total_chunks]).
 struct Seq {
   int64_t tok0;   // first token row
   int len;        // tokens
@@ -101,7 +104,7 @@ __device__ __forceinline__ Seq seq_of(const Params &p, int i) {
     s.len = b - a;
     s.chunk0 = ca;
     s.nchunks = cb - ca;
-    s.ok = (a >= 0) && (s.len >= 0) && (ca >= 0) && (cb <= p.total_chunks) &&
+    s.ok = (a >= 0) && (s.len >= 0) && (b <= p.T) && (ca >= 0) && (cb <= p.total_chunks) &&
            (s.nchunks == (s.len + kChunk - 1) / kChunk) && (s.nchunks <= p.max_chunks);
   }
   return s;

@@ -10,7 +10,10 @@
 //   G_r    = sum_{j<=r} g_j
 //   L[r,s] = beta_r exp(G_r - G_s) (k_r . k_s)        (s < r, else 0)
 //   T'     = (I + L)^-1 diag(beta)                     (the UT transform)
-// so that U = T' V and W = T' diag(exp(G)) K.
+// so that U = T' V and W = T' diag(exp(G)) K.  With the keys normalised to
+// unit length (k_r / |k_r|), K stays the exact bf16 operand of the Gram and
+// the row scales sk_r = 1/|k_r| multiply its result in float32:
+//   L[r,s] = beta_r exp(G_r - G_s) sk_r sk_s (k_r . k_s).
 // T = (I+L)^-1 by blocks: for a unit lower-triangular [[A, 0], [C, D]], the
 // inverse is [[A^-1, 0], [-D^-1 C A^-1, D^-1]].
 //   * lane t scans g;
@@ -22,8 +25,9 @@
 //     left 32x32 block, by the formula above on MFMA, transposed, every
 //     operand split into bf16 hi + lo (three products each, ~2^-17 relative
 //     error);
-//   * T' = T diag(beta), rounded to float16 (11 significant bits: the spine
-//     splits each value exactly into bf16 hi + lo), in the A-operand fragment
+//   * T' = T diag(beta), split into bf16 hi + lo (hi = bf16(x), lo =
+//     bf16(x - hi): ~2^-17 relative, what the spine's products of T' with the
+//     split R use), in the A-operand fragment
 //     order of the spine: fragment f = tri_frag(mt, kb) (mt >= 2kb) holds, in
 //     lane 16q + r, row t = 16mt + r, columns s = 32kb + 4q + e and
 //     32kb + 16 + 4q + e (e = 0..3).  In the diagonal fragments (mt = 2kb)
@@ -51,12 +55,49 @@ constexpr int kTP = 20;
 constexpr int kTileF = 16 * kTP + 4;
 __host__ __device__ constexpr int tri_tile(int mr, int ms) { return mr * (mr + 1) / 2 + ms; }
 
-// LDS workspace of one solving wave (6.9 KB).
+// LDS workspace of one solving wave (7.2 KB).
 struct __align__(16) UtWork {
   float D[5 * kTileF]; // tiles 0..3: (b, b); tile 4: T(1, 0)
   float Gs[kChunk];    // log2(e) G_t, for exp2
   float Bs[kChunk];    // beta_t
+  float Sk[kChunk];    // 1/|k_t| (normalised keys only)
 };
+
+// Sum of squares of the eight bf16 values of x, added to acc (four bf16 dot
+// products with float32 accumulation).  Each 32-bit word is copied to a
+// scalar before the bit cast: hipcc compiles a bit cast of a vector element
+// w[e] to element 0 for every e.
+__device__ __forceinline__ float sumsq8(const bf16x8 &x, float acc) {
+  const u32x4 w = __builtin_bit_cast(u32x4, x);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t we = w[e];
+    const bf16x2 p = __builtin_bit_cast(bf16x2, we);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
+}
+
+// 1/|x| of the chunk row `lane` from row fragments f[m][kb] (as load_k_frags
+// leaves them: lane 16q + r holds row 16m + r, columns 32kb + 8q .. +7): the
+// row's 128 squares are summed over a lane's 32 values, then over the four
+// lanes q = 0..3 that share r.  A row whose squares sum to 0 (or underflow)
+// gets 0, so that the normalised row is 0.
+__device__ __forceinline__ float inv_row_norm(const bf16x8 (&f)[4][4], int lane) {
+  float ps[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float a = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) a = sumsq8(f[m][kb], a);
+    a += __shfl_xor(a, 16, 64);
+    a += __shfl_xor(a, 32, 64);
+    ps[m] = a;
+  }
+  const int q4 = lane >> 4;
+  const float own = q4 == 0 ? ps[0] : q4 == 1 ? ps[1] : q4 == 2 ? ps[2] : ps[3];
+  return own > 0.f ? rsqrtf(own) : 0.f;
+}
 
 // hi = bf16(x), lo = bf16(x - hi) for pairs of floats; x - hi is exact in
 // float32 and comes from one bf16 dot product, (hi0, hi1) . (-1, 0) + x0, with
@@ -109,18 +150,14 @@ __device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[4][4], const uint16_t 
   }
 }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-// Two floats -> two float16 (round to nearest even), a in the low half.
-__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
-}
-
 // Gate scan and UT solve of one chunk by one wave.  In: kf (above), gv / bv
-// the g and beta of token `lane` (0 for lanes >= n).  Out: G = G_lane (lanes
-// past the end repeat G_{n-1}), Gn = G_{n-1}, and T' as tx[f] (8 float16 per
-// lane, f = 0..5).  W is private to the wave for the call.
-__device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, float bv, int n, UtWork &W,
-                                         int lane, u32x4 (&tx)[kTpFrags], float &G, float &Gn) {
+// the g and beta of token `lane` (0 for lanes >= n), skv its key scale
+// 1/|k_lane| (read only with kNorm).  Out: G = G_lane (lanes past the end
+// repeat G_{n-1}), Gn = G_{n-1}, and T' as tx[f] (bf16 hi, 8 per lane,
+// f = 0..5) and tx[6 + f] (bf16 lo).  W is private to the wave for the call.
+template <bool kNorm>
+__device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, float bv, float skv, int n,
+                                         UtWork &W, int lane, u32x4 (&tx)[2 * kTpFrags], float &G, float &Gn) {
   const int q4 = lane >> 4, r16 = lane & 15;
   const SplitK sp;
   auto dt = [&](int b) -> float * { return W.D + b * kTileF; };
@@ -142,6 +179,7 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
   Gn = __shfl(G, n - 1, 64);
   W.Gs[lane] = G * 1.4426950408889634f; // log2(e) G, for exp2 below
   W.Bs[lane] = bv;
+  if (kNorm) W.Sk[lane] = skv;
 
   // ---- L = strict_lower(diag(beta) (D * K K^T)) as C fragments (lane: column
   // 16ms + r, rows 16mr + 4q .. +3); the diagonal tiles go to LDS -----------
@@ -149,7 +187,8 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
 #pragma unroll
   for (int mr = 0; mr < 4; ++mr) {
     const f32x4 gr = *reinterpret_cast<const f32x4 *>(W.Gs + 16 * mr + 4 * q4);
-    const f32x4 br = *reinterpret_cast<const f32x4 *>(W.Bs + 16 * mr + 4 * q4);
+    f32x4 br = *reinterpret_cast<const f32x4 *>(W.Bs + 16 * mr + 4 * q4);
+    if (kNorm) br *= *reinterpret_cast<const f32x4 *>(W.Sk + 16 * mr + 4 * q4); // beta_r sk_r
 #pragma unroll
     for (int ms = 0; ms <= mr; ++ms) {
       f32x4 acc = zero4();
@@ -157,6 +196,7 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
       for (int kb = 0; kb < 4; ++kb) acc = mfma(kf[mr][kb], kf[ms][kb], acc);
       const int sc = 16 * ms + r16;
       const float gs = W.Gs[sc];
+      if (kNorm) acc *= W.Sk[sc]; // sk_s
       f32x4 l;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -265,18 +305,21 @@ __device__ __forceinline__ void ut_solve(const bf16x8 (&kf)[4][4], float gv, flo
     }
   }
 
-  // ---- T' = T diag(beta), float16, in fragment order: fragment (mt, kb) is
-  // row 16mt + r, columns 32kb + 4q .. and 32kb + 16 + 4q .. ----------------
+  // ---- T' = T diag(beta), bf16 hi + lo, in fragment order: fragment (mt, kb)
+  // is row 16mt + r, columns 32kb + 4q .. and 32kb + 16 + 4q .. -------------
   auto emit = [&](int f, int kb, const f32x4 &a, const f32x4 &b, bool two) {
     const int s0 = 32 * kb + 4 * q4;
     const f32x4 x = a * *reinterpret_cast<const f32x4 *>(W.Bs + s0);
-    u32x4 out = {cvt_pk_f16(x[0], x[1]), cvt_pk_f16(x[2], x[3]), 0u, 0u};
+    uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+    sp.pair(x[0], x[1], hi[0], lo[0]);
+    sp.pair(x[2], x[3], hi[1], lo[1]);
     if (two) {
       const f32x4 y = b * *reinterpret_cast<const f32x4 *>(W.Bs + s0 + 16);
-      out[2] = cvt_pk_f16(y[0], y[1]);
-      out[3] = cvt_pk_f16(y[2], y[3]);
+      sp.pair(y[0], y[1], hi[2], lo[2]);
+      sp.pair(y[2], y[3], hi[3], lo[3]);
     }
-    tx[f] = out;
+    tx[f] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    tx[kTpFrags + f] = u32x4{lo[0], lo[1], lo[2], lo[3]};
   };
   emit(tri_frag(0, 0), 0, row4(dt(0)), zero4(), false);
   emit(tri_frag(1, 0), 0, Rt[0], row4(dt(1)), true);

@@ -28,15 +28,17 @@
 //     active pair stages chunk c+1 into the free half of a double-buffered
 //     LDS stage, from registers it filled two steps earlier, then fetches
 //     chunk c+3: role 0 the Q and K rows (1 KB per load), role 1 the T'
-//     fragments (float16, split into bf16 hi + lo as they are staged),
-//     decays, gate sums and V rows.  The idle pair works on chunk c, visible
+//     fragments (bf16 hi + lo), the
+//     gate sums G (from which it forms the decays as it stages them; with q/k
+//     normalisation the row scales too) and V rows.  The idle pair works on chunk c, visible
 //     in the stage compute reads: role 1 reads the Q and K row fragments and
 //     forms the causal decayed scores A of chunk c on MFMA (for S = 4 role 0
 //     forms half of them); role 0 stores the output tile of chunk c-2.
 //     The compute waves read K^T and their V tiles out of the row tiles with
 //     transposing LDS reads.
-// One barrier per chunk (and one after the last).  Entry states leave as
-// 16-byte pieces (dk order perm_dk).  The output is formed transposed, so a
+// One barrier per chunk (and one after the last).  Entry states (when asked
+// for) leave as 16-byte pieces of [dv][dk] rows, straight from the bf16 h
+// fragments (dk order perm_dk).  The output is formed transposed, so a
 // lane holds 8-byte pieces of token rows; they are gathered per chunk in an
 // LDS tile and stored by a loader as whole row segments of the workgroup's
 // columns.
@@ -45,15 +47,14 @@
 // ends the reading step.
 // Precision: h is float32 between chunks; h, R and the decayed uc are split
 // into bf16 hi+lo for the products that feed the state (K is exact in bf16;
-// T', stored in float16, splits exactly), so every product keeps ~2^-17
-// relative error with bf16 MFMA and float32 accumulation, on top of T''s own
-// float16 rounding (2^-11).  The output uses bf16(h) and bf16(uc) -- the
+// T' arrives as a bf16 hi + lo pair), so every product keeps ~2^-17
+// relative error with bf16 MFMA and float32 accumulation.  The output uses bf16(h) and bf16(uc) -- the
 // page's stage 3 reads both in bf16 -- with float32 accumulation.
 //
 // Workgroup order: all workgroups that read one k-head's rows (its r v-heads
 // x column groups) get the same blockIdx.x % 8, so that on a round-robin XCD
 // dispatch they share one XCD's L2.
-#include "gdn_ut_solve.h" // SplitK
+#include "gdn_device.h"
 
 namespace gdn {
 
@@ -89,17 +90,51 @@ __device__ __forceinline__ u32x2 read_tr(const void *lds_base, int byte_off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)a));
 }
 
+// Section stamps (profiling build only): every wave reads the shader clock
+// (s_memtime) at its section marks into registers, and the 100 MHz clock
+// (s_memrealtime) once per step; after the step's barrier, lane 0 of each wave
+// of workgroup 0 stores the marks of steps kStampFirst.. (one row of
+// kStampSlots per step, mark 15 the 100 MHz stamp).  The marks add no branch
+// and no wait inside a step: the results are first used by the store after
+// the barrier.  In the product build the marks are empty.
+#ifdef GDN_SECTION_STAMPS
+#define GDN_STAMP_DECL unsigned long long ts_[kStampSlots] = {}
+#define GDN_STAMP(id) (ts_[id] = __builtin_amdgcn_s_memtime())
+#define GDN_RSTAMP() (ts_[15] = __builtin_amdgcn_s_memrealtime())
+#define GDN_STAMP_FLUSH(c)                                                                                            \
+  do {                                                                                                                \
+    if (p.stamps && blockIdx.x == 0 && lane == 0 && (c) >= kStampFirst && (c) < kStampFirst + kStampSteps) {         \
+      _Pragma("unroll") for (int id_ = 0; id_ < kStampSlots; ++id_)                                                  \
+          p.stamps[(size_t(wave) * kStampSteps + ((c) - kStampFirst)) * kStampSlots + id_] = ts_[id_];               \
+    }                                                                                                                 \
+  } while (0)
+#else
+#define GDN_STAMP_DECL
+#define GDN_STAMP(id) ((void)0)
+#define GDN_RSTAMP() ((void)0)
+#define GDN_STAMP_FLUSH(c) ((void)0)
+#endif
+
 template <int N> struct Mask {
   static constexpr int value = N;
 };
 
+// The per-token factors of a chunk, formed by the role-1 loader from G (and,
+// with q/k normalisation, the row scales sk = 1/|k_t|, sq = 1/|q_t|; without
+// it both are 1): the normalised keys and queries are diag(sk) K and
+// diag(sq) Q, so every product keeps the exact bf16 rows and the scales ride
+// on factors that are applied anyway.
 struct Stage {
   u32x4 kr[64 * 16];          // K rows: row fragments for K h and the scores, K^T for K^T uc
   u32x4 qr[64 * 16];          // Q rows: row fragments for Q h and the scores
   u32x4 tp[2 * kTpFrags * 64]; // T' fragments: 6 hi, then 6 lo
   u32x4 vr[64 * 8];           // V rows, the workgroup's columns
-  float dec[2 * kChunk];      // exp(G_t), exp(G_{n-1} - G_t)
-  float g2[kChunk];           // log2(e) G_t, for the scores' decays
+  float eg[kChunk];           // exp(G_t) sk_t:       R = V - diag(eg) (K h)
+  float dn[kChunk];           // exp(G_n - G_t) sk_t: h += K^T diag(dn) uc
+  float dq[kChunk];           // exp(G_t) sq_t:       O = diag(dq) (Q h) + A uc
+  float g2q[kChunk];          // log2(e) G_t + log2(sq_t) \ A[t][s] = exp2(g2q_t - g2k_s) q_t.k_s
+  float g2k[kChunk];          // log2(e) G_s - log2(sk_s) /
+  float en[4];                // en[0] = exp(G_n), G_n the gate sum at the last token
 };
 
 // Split two C tiles (a k block of 32 rows, chain order) into hi / lo bf16
@@ -124,7 +159,7 @@ __device__ __forceinline__ void split_tiles(const f32x4 &t0, const f32x4 &t1, ui
   lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
-template <int kStrips>
+template <int kStrips, bool kEntry>
 __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params p) {
   constexpr int kGroups = 8 / kStrips; // workgroups per chain
   // ---- which (sequence, v-head, column group) ----------------------------
@@ -171,7 +206,8 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 
     // scores of the chunk staged in S, into A: C(ms, mt)[s][t] = q_t . k_s
     // (A = K rows s, B = Q rows t; lane holds column t = 16mt + r16, rows
-    // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s);
+    // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s)
+    // (times sq_t sk_s with q/k normalisation);
     // two vertically stacked tiles are the chain-order A fragment (mt, kb).
     // Only the fragments of the row blocks mt in the bit mask are formed (the
     // caller passes Mask<bits>).
@@ -206,10 +242,10 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       for (int mt = 0; mt < 4; ++mt) {
         if (!(mask & (1 << mt))) continue;
         const int t = 16 * mt + r16;
-        const float g2t = S.g2[t];
+        const float g2t = S.g2q[t];
 #pragma unroll
         for (int ms = 0; ms <= mt; ++ms) {
-          const f32x4 g2s = *reinterpret_cast<const f32x4 *>(S.g2 + 16 * ms + 4 * q4);
+          const f32x4 g2s = *reinterpret_cast<const f32x4 *>(S.g2k + 16 * ms + 4 * q4);
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int si = 16 * ms + 4 * q4 + ii;
@@ -224,6 +260,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         }
       }
     };
+    GDN_STAMP_DECL;
     if (role == 0) {
       // ---- Q, K rows; outputs --------------------------------------------
       u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
@@ -272,41 +309,52 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       }
       __syncthreads();
       for (int c = 0; c <= nch; ++c) {
+        GDN_STAMP(0);
         if (((c + 1) & 1) == pair && c + 1 < nch) {
           stash(st[(c + 1) & 1]);
+          GDN_STAMP(1);
           if (c + 3 < nch) fetch(c + 3);
+          GDN_STAMP(2);
         }
         // the idle pair stores the output of chunk c-2 and, for S = 4, forms
         // half of chunk c's scores
         if ((c & 1) == pair && c >= 2) store_out(c - 2);
         if (kStrips == 4 && (c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<0x9>());
+        GDN_STAMP(3);
         __syncthreads();
+        GDN_STAMP(4);
+        GDN_STAMP_FLUSH(c);
       }
       // after the last barrier: the last chunk's output
       if ((nch & 1) == pair) store_out(nch - 1);
       return;
     }
 
-    // ---- T', decays, gate sums, V rows; scores ------------------------------
-    u32x4 t16[kTpFrags];     // T' as fetched, float16
-    u32x4 tx[2 * kTpFrags];  // T' as staged: bf16 hi (f), lo (6 + f)
-    float d0 = 0.f, d1 = 0.f, gg = 0.f;
+    // ---- T', gate sums (and row scales), V rows; scores ---------------------
+    const bool norm = (p.opts & kOptNorm) != 0;
+    u32x4 tx[2 * kTpFrags];  // T' as fetched and staged: bf16 hi (f), lo (6 + f)
+    float gg = 0.f, skv = 1.f, sqv = 1.f;
     u32x4 vx[kVPieces];
     auto fetch = [&](int c) __attribute__((always_inline)) {
       const int64_t sl = slot_of(p, s, h, c);
       const char *tsrc = reinterpret_cast<const char *>(p.tp) + sl * kTpBytes;
 #pragma unroll
-      for (int f = 0; f < kTpFrags; ++f) {
-        if (tp_half(f)) { // the zero half above the diagonal is not stored
-          const u32x2 x = *reinterpret_cast<const u32x2 *>(tsrc + tp_offset(f) + 8 * lane);
-          t16[f] = u32x4{x[0], x[1], 0u, 0u};
-        } else {
-          t16[f] = *reinterpret_cast<const u32x4 *>(tsrc + tp_offset(f) + 16 * lane);
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int f = 0; f < kTpFrags; ++f) {
+          const char *src = tsrc + part * kTpHalfBytes + tp_offset(f);
+          if (tp_half(f)) { // the zero half above the diagonal is not stored
+            const u32x2 x = *reinterpret_cast<const u32x2 *>(src + 8 * lane);
+            tx[part * kTpFrags + f] = u32x4{x[0], x[1], 0u, 0u};
+          } else {
+            tx[part * kTpFrags + f] = *reinterpret_cast<const u32x4 *>(src + 16 * lane);
+          }
         }
-      }
-      d0 = p.dec[sl * 2 * kChunk + lane];
-      d1 = p.dec[sl * 2 * kChunk + kChunk + lane];
       gg = p.gc[sl * kChunk + lane];
+      if (norm) {
+        skv = p.nrm[sl * 2 * kChunk + lane];
+        sqv = p.nrm[sl * 2 * kChunk + kChunk + lane];
+      }
       const int nn = min(kChunk, s.len - c * kChunk);
       const char *vc = reinterpret_cast<const char *>(p.v + (s.tok0 + int64_t(c) * kChunk) * p.v_row + int64_t(h) * kDim + col0);
       const uint32_t pitch = uint32_t(p.v_row) * 2u;
@@ -316,56 +364,50 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         vx[jj] = *reinterpret_cast<const u32x4 *>(vc + off);
       }
     };
-    // float16 T' -> bf16 hi + lo, exactly: 11 significant bits leave at most
-    // 3 for x - hi
-    auto decode = [&]() __attribute__((always_inline)) {
-      const SplitK sp;
-#pragma unroll
-      for (int f = 0; f < kTpFrags; ++f) {
-        uint32_t hw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int w = 0; w < (tp_half(f) ? 2 : 4); ++w) {
-          const uint32_t x = t16[f][w];
-          const float a = float(__builtin_bit_cast(_Float16, uint16_t(x & 0xFFFFu)));
-          const float b = float(__builtin_bit_cast(_Float16, uint16_t(x >> 16)));
-          sp.pair(a, b, hw[w], lw[w]);
-        }
-        tx[f] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-        tx[kTpFrags + f] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-      }
-    };
+    // the chunk's per-token factors from G (rows past the sequence end repeat
+    // the last G, so lane 63 holds G_n)
     auto stash = [&](Stage &S) __attribute__((always_inline)) {
 #pragma unroll
       for (int f = 0; f < 2 * kTpFrags; ++f) S.tp[f * 64 + lane] = tx[f];
-      S.dec[lane] = d0;
-      S.dec[kChunk + lane] = d1;
-      S.g2[lane] = gg * 1.4426950408889634f; // log2(e) G
+      const float Gn = __shfl(gg, kChunk - 1, 64);
+      const float e = expf(gg), en = expf(Gn - gg);
+      const float g2 = gg * 1.4426950408889634f; // log2(e) G
+      S.eg[lane] = e * skv;
+      S.dn[lane] = en * skv;
+      S.dq[lane] = e * sqv;
+      S.g2q[lane] = norm ? g2 + log2f(sqv) : g2;
+      S.g2k[lane] = norm ? g2 - log2f(skv) : g2;
+      if (lane == kChunk - 1) S.en[0] = e;
 #pragma unroll
       for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
     if (pair < nch) fetch(pair);
     if (pair == 0) {
-      decode();
       stash(st[0]);
       if (2 < nch) fetch(2);
     }
     __syncthreads();
     for (int c = 0; c <= nch; ++c) {
-      // the active pair splits the T' it fetched two steps earlier and
-      // stages chunk c+1
+      GDN_STAMP(0);
+      // the active pair stages chunk c+1, fetched two steps earlier
       if (((c + 1) & 1) == pair && c + 1 < nch) {
-        decode();
         stash(st[(c + 1) & 1]);
+        GDN_STAMP(1);
         if (c + 3 < nch) fetch(c + 3);
+        GDN_STAMP(2);
       }
       // the idle pair forms the scores of chunk c (with role 0 for S = 4)
       if ((c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<kStrips == 4 ? 0x6 : 0xF>());
+      GDN_STAMP(3);
       __syncthreads();
+      GDN_STAMP(4);
+      GDN_STAMP_FLUSH(c);
     }
     return;
   }
 
   // =========================== compute waves ==============================
+  GDN_STAMP_DECL;
   const int colw = col0 + 16 * wave; // this wave's strip
   float *hp = state_of(p, i, h);
   f32x4 H[8]; // H[m][ii] = h[perm_dk(16m + 4q + ii)][colw + r16]
@@ -435,9 +477,13 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   // output's products (the previous chunk's A uc, this chunk's Q h) filling
   // the split of h.  Scheduling barriers keep the sections in this order.
   for (int c = 0; c < nch; ++c) {
+    GDN_RSTAMP();
+    GDN_STAMP(0);
     const Stage &S = st[c & 1];
     const int64_t sl = slot_of(p, s, h, c);
-    uint16_t *sdst = p.s_entry + sl * (kDim * kDim) + (colw + r16) * kDim + 8 * q4;
+    // entry state: this lane's bf16 h fragments are 8 consecutive dk of column
+    // colw + r16, so they leave as 16-byte pieces of the [dv][dk] rows
+    uint16_t *edst = kEntry ? p.s_entry + sl * (kDim * kDim) + (colw + r16) * kDim + 8 * q4 : nullptr;
 
     // ---- h -> hi/lo (chain order over dk, eight consecutive dk per lane);
     // bf16(h) is the entry state.  The previous chunk's output, then Q h, the
@@ -450,7 +496,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       for (int mt = 0; mt < 2; ++mt) kA[kb][mt] = rfrag(S.kr, mt, kb);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) qa[0][mt] = rfrag(S.qr, mt, 0);
-    const float en = S.dec[kChunk - 1]; // exp(G) of the last row = exp(G_n): rows past the end repeat it
+    const float en = S.en[0]; // exp(G_n)
     if (c > 0) {
       bf16x8 af[kTpFrags];
       load_scores(c - 1, af);
@@ -462,8 +508,9 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     Hn[0] = H[0] * en;
     Hn[1] = H[1] * en;
     split_tiles(H[0], H[1], m0, m1, Hh[0], Hl[0]);
-    *reinterpret_cast<u32x4 *>(sdst) = __builtin_bit_cast(u32x4, Hh[0]);
+    if (kEntry) *reinterpret_cast<u32x4 *>(edst) = __builtin_bit_cast(u32x4, Hh[0]);
     __builtin_amdgcn_sched_barrier(0);
+    GDN_STAMP(1);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) O[mt] = zero4();
 #pragma unroll
@@ -478,11 +525,12 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         Hn[2 * kb + 2] = H[2 * kb + 2] * en;
         Hn[2 * kb + 3] = H[2 * kb + 3] * en;
         split_tiles(H[2 * kb + 2], H[2 * kb + 3], m0, m1, Hh[kb + 1], Hl[kb + 1]);
-        *reinterpret_cast<u32x4 *>(sdst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
+        if (kEntry) *reinterpret_cast<u32x4 *>(edst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
         GDN_INTERLEAVE(4, 5, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    GDN_STAMP(2);
 
     // ---- K h, half A (rows 0..31), while h is scaled by exp(G_n) ----------
     bf16x8 kB[4][2];
@@ -494,7 +542,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     u32x2 vv[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      eg[mt] = *reinterpret_cast<const f32x4 *>(S.dec + 16 * mt + 4 * q4);
+      eg[mt] = *reinterpret_cast<const f32x4 *>(S.eg + 16 * mt + 4 * q4);
       // V[16mt + 4q + ii][colw + r16], ii = 0..3: a transposing read of the V rows
       vv[mt] = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
     }
@@ -508,6 +556,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       }
     GDN_INTERLEAVE(16, 2, 1);
     __builtin_amdgcn_sched_barrier(0);
+    GDN_STAMP(3);
 
     // ---- K h, half B, while R = V - diag(exp(G)) K h of half A is formed ---
     bf16x8 th[kTpFrags], tl[kTpFrags];
@@ -538,6 +587,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     split_tiles(R[0], R[1], m0, m1, Rh[0], Rl[0]);
     GDN_INTERLEAVE(16, 3, 2);
     __builtin_amdgcn_sched_barrier(0);
+    GDN_STAMP(4);
 
     // ---- uc = T' R: half A (rows 0..31) and the R-A part of half B, while R
     // of half B is formed ----------------------------------------------------
@@ -552,8 +602,8 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     float dq[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      dn[mt] = *reinterpret_cast<const f32x4 *>(S.dec + kChunk + 16 * mt + 4 * q4);
-      dq[mt] = S.dec[16 * mt + r16];
+      dn[mt] = *reinterpret_cast<const f32x4 *>(S.dn + 16 * mt + 4 * q4);
+      dq[mt] = S.dq[16 * mt + r16];
     }
     f32x4 D[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -567,6 +617,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     split_tiles(R[2], R[3], m0, m1, Rh[1], Rl[1]);
     GDN_INTERLEAVE(12, 3, 3);
     __builtin_amdgcn_sched_barrier(0);
+    GDN_STAMP(5);
 
     // ---- uc half B (R-B part), while half A of uc is rounded for the output,
     // decayed and split; the output's state term is scaled ------------------
@@ -588,6 +639,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     for (int mt = 0; mt < 4; ++mt) O[mt] *= dq[mt];
     GDN_INTERLEAVE(6, 6, 4);
     __builtin_amdgcn_sched_barrier(0);
+    GDN_STAMP(6);
 
     // ---- h += K^T diag(exp(G_n - G)) uc, half A, while half B of uc is
     // rounded, decayed and split --------------------------------------------
@@ -605,6 +657,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     split_tiles(D[2], D[3], m0, m1, Dh[1], Dl[1]);
     GDN_INTERLEAVE(16, 2, 5);
     __builtin_amdgcn_sched_barrier(0);
+    GDN_STAMP(7);
 
     // ---- h += ..., half B --------------------------------------------------
 #pragma unroll
@@ -614,8 +667,11 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     }
 #pragma unroll
     for (int m = 0; m < 8; ++m) H[m] = Hn[m];
+    GDN_STAMP(8);
 
     __syncthreads();
+    GDN_STAMP(9);
+    GDN_STAMP_FLUSH(c);
   }
   // the last chunk's output: its scores were formed in the last step
   {
@@ -649,7 +705,10 @@ hipError_t launch_with(const Params &p, hipStream_t stream) {
   const int r = p.nv / p.nk;
   const int kgroups = p.B * p.nk;
   const int blocks = 8 * ((kgroups + 7) / 8) * r * (8 / kStrips);
-  hipLaunchKernelGGL(chunk_delta_h_fwd_o<kStrips>, dim3(blocks), dim3((kStrips + 4) * 64), 0, stream, p);
+  if (p.opts & kOptEntry)
+    hipLaunchKernelGGL((chunk_delta_h_fwd_o<kStrips, true>), dim3(blocks), dim3((kStrips + 4) * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_delta_h_fwd_o<kStrips, false>), dim3(blocks), dim3((kStrips + 4) * 64), 0, stream, p);
   return hipGetLastError();
 }
 } // namespace

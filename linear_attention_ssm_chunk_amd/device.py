@@ -11,7 +11,7 @@ import torch
 from . import binding as B
 from .inputs import CHUNK, HEAD_DIM, pack_contiguous, pack_conv
 
-TP_ELEMS = 2560  # float16 elements of a slot's T' (include/gdn_prefill.h)
+TP_ELEMS = 2560  # bf16 elements of each part (hi, lo) of a slot's T' (include/gdn_prefill.h)
 
 
 def _to_bf16_tensor(u16, device):
@@ -35,11 +35,15 @@ class DeviceProblem:
              "table"      -- one allocation per sequence, passed as a pointer table
     ragged : None picks dense mode when every sequence has the same length,
              True forces cu_seqlens / cu_chunks.
+    flags  : GDN_OPT_* options of the calls (default: entry states emitted,
+             q and k passed normalised).
     """
 
-    def __init__(self, p, layout="contiguous", state="contiguous", ragged=None, device="cuda"):
+    def __init__(self, p, layout="contiguous", state="contiguous", ragged=None, device="cuda",
+                 flags=B.GDN_OPT_ENTRY_STATES):
         self.p = p
         self.device = device
+        self.flags = int(flags)
         self.nseq, self.nk, self.nv = p.nseq, p.nk, p.nv
         self.N = p.n_tokens
         lens = p.lengths
@@ -76,7 +80,8 @@ class DeviceProblem:
             nch = np.diff(self.cu_chunks_host)
             max_c, total_c = (int(nch.max()) if len(nch) else 0), int(self.cu_chunks_host[-1])
             # the library trusts device offsets; check the host copies once here
-            if B.gdn_varlen_check_host(self.nseq, self.cu_seqlens_host, self.cu_chunks_host, max_c, total_c) != B.GDN_OK:
+            if B.gdn_varlen_check_host(self.nseq, self.N, self.cu_seqlens_host, self.cu_chunks_host, max_c,
+                                       total_c) != B.GDN_OK:
                 raise ValueError(B.gdn_last_error())
             self.varlen = B.gdn_varlen(self._cu_s.data_ptr(), self._cu_c.data_ptr(), max_c, total_c)
             self.B, self.T = self.nseq, self.N
@@ -97,13 +102,13 @@ class DeviceProblem:
         self.reset_state()
 
         self.out = torch.empty((self.N, self.nv, HEAD_DIM), dtype=torch.bfloat16, device=device)
-        self.scratch_bytes = B.gdn_prefill_scratch_bytes(self.B, self.T, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
-                                                         self.varlen)
+        self.scratch_bytes = B.gdn_prefill_scratch_bytes_ex(self.B, self.T, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
+                                                            self.varlen, self.flags)
         if self.scratch_bytes == 0:
             raise ValueError("invalid sizes for the scratch layout")
         self.scratch = torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
-        self.layout_info = B.gdn_prefill_scratch_layout(self.B, self.T, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
-                                                        self.varlen)
+        self.layout_info = B.gdn_prefill_scratch_layout_ex(self.B, self.T, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
+                                                           self.varlen, self.flags)
 
     # -- state ---------------------------------------------------------------
     def reset_state(self):
@@ -135,11 +140,11 @@ class DeviceProblem:
 
     def run(self, stream=None):
         s = current_stream_handle() if stream is None else stream
-        return B.gdn_prefill(*self.args(), s)
+        return B.gdn_prefill_ex(*self.args(), self.flags, s)
 
     def run_stage(self, stage, stream=None):
         s = current_stream_handle() if stream is None else stream
-        return B.gdn_prefill_stage(stage, *self.args(), s)
+        return B.gdn_prefill_stage_ex(stage, *self.args(), self.flags, s)
 
     def decode_step(self, t, out=None, stream=None):
         """One gdn_decode call on token t of every sequence (dense problems, all
@@ -177,12 +182,14 @@ class DeviceProblem:
         L = self.layout_info
         S = int(L.slots)
         off = getattr(L, name)
+        if off == B.GDN_NO_REGION:
+            raise KeyError(f"region {name} is not in this layout (flags 0x{self.flags:x})")
         if name == "gc":
             return self.scratch[off:off + S * CHUNK * 4].view(torch.float32).view(S, CHUNK)
-        if name == "dec":
+        if name == "nrm":
             return self.scratch[off:off + S * 2 * CHUNK * 4].view(torch.float32).view(S, 2, CHUNK)
         if name == "tp":
-            return self.scratch[off:off + S * TP_ELEMS * 2].view(torch.float16).view(S, TP_ELEMS)
+            return self.scratch[off:off + S * 2 * TP_ELEMS * 2].view(torch.bfloat16).view(S, 2, TP_ELEMS)
         if name == "s_entry":
             return self.scratch[off:off + S * HEAD_DIM * HEAD_DIM * 2].view(torch.bfloat16).view(S, HEAD_DIM, HEAD_DIM)
         raise KeyError(name)

@@ -13,6 +13,8 @@ Recipe (fixed, documented in the design notes):
     be drawn in parallel and the result does not depend on thread count).
   * q, k ~ N(0, 1) float32, L2-normalised per (token, head) 128-vector in
     float32, then rounded to bf16 (round-to-nearest-even); v ~ N(0, 1) -> bf16.
+    With ``raw_qk`` q and k are left as drawn (N(0, 1) -> bf16), for calls
+    that normalise them inside the library.
   * g = -softplus(N(0, 1)) float32 (via logaddexp); beta = sigmoid(N(0, 1))
     float32.
   * h0 ~ N(0, 0.02^2) float32 where the workload has a carried state, else 0.
@@ -132,19 +134,25 @@ def _unit_rows_bf16(rng, shape):
     return f32_to_bf16_bits(x)
 
 
-def make_problem(lengths, nk, nv, seed, h0="normal"):
+def _raw_rows_bf16(rng, shape):
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def make_problem(lengths, nk, nv, seed, h0="normal", raw_qk=False):
     """Draw q, k, v, g, beta, h0 for the given sequence lengths.
 
     ``SeedSequence(seed).spawn(6)`` gives one stream per array in the order q,
     k, v, g, beta, h0; the per-token arrays are drawn in blocks of 4096 tokens,
-    block b from child b of the array's stream."""
+    block b from child b of the array's stream.  ``raw_qk``: q and k as drawn,
+    not normalised."""
     from concurrent.futures import ThreadPoolExecutor
     import os
     N = int(sum(lengths))
     ss = np.random.SeedSequence(seed).spawn(6)
     with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as pool:
-        q = _fill(ss[0], N, lambda r, n: _unit_rows_bf16(r, (n, nk, HEAD_DIM)), pool)
-        k = _fill(ss[1], N, lambda r, n: _unit_rows_bf16(r, (n, nk, HEAD_DIM)), pool)
+        rows = _raw_rows_bf16 if raw_qk else _unit_rows_bf16
+        q = _fill(ss[0], N, lambda r, n: rows(r, (n, nk, HEAD_DIM)), pool)
+        k = _fill(ss[1], N, lambda r, n: rows(r, (n, nk, HEAD_DIM)), pool)
         v = _fill(ss[2], N, lambda r, n: f32_to_bf16_bits(r.standard_normal((n, nv, HEAD_DIM), dtype=np.float32)),
                   pool)
         g = _fill(ss[3], N, lambda r, n: (-np.logaddexp(np.float32(0), r.standard_normal((n, nv), dtype=np.float32))
@@ -162,17 +170,19 @@ def make_problem(lengths, nk, nv, seed, h0="normal"):
     return Problem(list(lengths), nk, nv, q, k, v, g, beta, h, seed)
 
 
-def make_workload(index, seed=None):
+def make_workload(index, seed=None, raw_qk=False):
     """The synthetic problem of workload ``index`` (1..5) with seed = index
-    unless given.  The ragged workload searches seeds from the base seed."""
+    unless given.  The ragged workload searches seeds from the base seed.
+    ``raw_qk``: q and k left unnormalised (for calls that normalise them)."""
     w = WORKLOADS[index]
     seed = index if seed is None else seed
     if "nseq" in w:
         lengths, used = ragged_lengths(seed, w["nseq"])
-        p = make_problem(lengths, w["nk"], w["nv"], used, w["h0"])
+        p = make_problem(lengths, w["nk"], w["nv"], used, w["h0"], raw_qk=raw_qk)
         p.meta["length_seed"] = used
     else:
-        p = make_problem([w["T"]] * w["B"], w["nk"], w["nv"], seed, w["h0"])
+        p = make_problem([w["T"]] * w["B"], w["nk"], w["nv"], seed, w["h0"], raw_qk=raw_qk)
+    p.meta["raw_qk"] = raw_qk
     p.meta.update(w)
     p.meta["index"] = index
     return p

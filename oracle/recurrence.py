@@ -4,14 +4,15 @@ TEST INFRASTRUCTURE ONLY (see the package docstring): imported by tests,
 ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg, never by the
 product path.
 
-Gated DeltaNet (Yang, Kautz & Hatamizadeh, "Gated Delta Networks: Improving
-Mamba2 with Delta Rule", ICLR 2025), per value head:
+The gated delta rule (Gated DeltaNet), per value head:
 
     S_t = exp(g_t) * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
     o_t = S_t q_t
 
-with S in R^{dv x dk}.  The page "spark_model/layers/ops/ssm_gdn_a3.rs" names
-this method (GDN, gated_delta_rule) and stores the state as ``[kd][vd]``
+with S in R^{dv x dk}.  This is the method the page
+"spark_model/layers/ops/ssm_gdn_a3.rs" runs as its GDN prefill (its kernels
+are the gated_delta_rule_chunk_* family, its stages listed in the doc comment
+of ``gdn_prefill_fla``); the page stores the state as ``[kd][vd]``
 (comment on ``h_state_is_table``), i.e. ``h = S^T``; inputs and outputs of this
 module use that stored orientation, the loop itself uses S.
 

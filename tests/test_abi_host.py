@@ -30,7 +30,9 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"gdn_prefill", "gdn_prefill_stage", "gdn_prefill_validate", "gdn_prefill_scratch_bytes",
-            "gdn_prefill_scratch_layout", "gdn_varlen_check_host", "gdn_last_error"} <= set(names)
+            "gdn_prefill_scratch_layout", "gdn_varlen_check_host", "gdn_last_error", "gdn_prefill_ex",
+            "gdn_prefill_stage_ex", "gdn_prefill_validate_ex", "gdn_prefill_scratch_bytes_ex",
+            "gdn_prefill_scratch_layout_ex", "gdn_decode", "gdn_decode_validate"} <= set(names)
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -119,6 +121,37 @@ def test_ragged_guards():
     assert rc == B.GDN_EINVAL and "max_chunks" in msg
     rc, msg = validate(varlen=B.gdn_varlen(P + 64, P + 128, 3, 4), T=300)
     assert rc == B.GDN_EINVAL and "cannot hold" in msg
+    # every chunk holds a token: more chunks than tokens is a bad table
+    rc, msg = validate(varlen=B.gdn_varlen(P + 64, P + 128, 3, 5), T=4)
+    assert rc == B.GDN_EINVAL and "exceeds T" in msg
+
+
+def test_ragged_call_without_tokens():
+    """T == 0 allows NULL token pointers only with no chunks at all: a table
+    that still claims chunks is rejected before anything could be launched on
+    NULL pointers."""
+    none = dict(q=0, k=0, v=0, g=0, beta=0, out=0, T=0)
+    vl0 = B.gdn_varlen(P + 64, P + 128, 0, 0)
+    rc, msg = validate(varlen=vl0, scratch_bytes=4096, **none)
+    assert rc == B.GDN_OK, msg
+    rc, msg = validate(varlen=B.gdn_varlen(P + 64, P + 128, 1, 1), scratch_bytes=1 << 20, **none)
+    assert rc == B.GDN_EINVAL and "exceeds T" in msg
+
+
+def test_flags_are_checked():
+    a = good_args()
+    args = [a[k] for k in ("q", "k", "v", "g", "beta", "h_state", "h_state_is_table", "out", "scratch",
+                           "scratch_bytes", "B", "T", "nk", "nv", "dk", "dv", "strides", "varlen")]
+    assert B.gdn_prefill_validate_ex(*args, B.GDN_OPT_ENTRY_STATES) == B.GDN_OK
+    assert B.gdn_prefill_validate_ex(*args, 0) == B.GDN_OK
+    assert B.gdn_prefill_validate_ex(*args, B.GDN_OPT_L2NORM_QK) == B.GDN_OK
+    assert B.gdn_prefill_validate_ex(*args, 0x4) == B.GDN_EINVAL
+    assert "flags=0x4" in B.gdn_last_error()
+    # the normalisation region needs scratch of its own
+    args[9] = B.gdn_prefill_scratch_bytes_ex(2, 200, 2, 4, 128, 128, None, 0)
+    assert B.gdn_prefill_validate_ex(*args, 0) == B.GDN_OK
+    assert B.gdn_prefill_validate_ex(*args, B.GDN_OPT_L2NORM_QK) == B.GDN_ESCRATCH
+    assert B.gdn_prefill_scratch_bytes_ex(2, 200, 2, 4, 128, 128, None, 0x8) == 0
 
 
 def test_prefill_rejects_without_touching_the_gpu():
@@ -139,11 +172,19 @@ def test_scratch_layout_arithmetic():
     L = B.gdn_prefill_scratch_layout(4, 8192, 16, 32, 128, 128)
     chunks = 4 * 128
     slots = chunks * 32
-    assert L.slots == slots and L.gc == 0
-    assert L.dec == slots * 64 * 4
-    assert L.tp == L.dec + slots * 2 * 64 * 4
-    assert L.s_entry == L.tp + slots * 2560 * 2
+    assert L.slots == slots and L.gc == 0 and L.flags == B.GDN_OPT_ENTRY_STATES
+    assert L.tp == slots * 64 * 4
+    assert L.nrm == B.GDN_NO_REGION
+    assert L.s_entry == L.tp + slots * 2 * 2560 * 2
     assert L.total == L.s_entry + slots * 128 * 128 * 2
+    # no entry states: gc and T' only; with normalisation the row scales follow T'
+    L0 = B.gdn_prefill_scratch_layout_ex(4, 8192, 16, 32, 128, 128, None, 0)
+    assert L0.s_entry == B.GDN_NO_REGION and L0.nrm == B.GDN_NO_REGION
+    assert L0.total == L.s_entry
+    Ln = B.gdn_prefill_scratch_layout_ex(4, 8192, 16, 32, 128, 128, None,
+                                         B.GDN_OPT_L2NORM_QK | B.GDN_OPT_ENTRY_STATES)
+    assert Ln.nrm == L.s_entry and Ln.s_entry == Ln.nrm + slots * 2 * 64 * 4
+    assert Ln.total == Ln.s_entry + slots * 128 * 128 * 2
     assert B.gdn_prefill_scratch_bytes(2, 0, 2, 4, 128, 128, B.gdn_varlen(P, P, 0, 0)) == 256
     # partial last chunk: T = 200 -> 4 chunks
     assert B.gdn_prefill_scratch_layout(1, 200, 1, 1, 128, 128).slots == 4
@@ -155,16 +196,20 @@ def test_scratch_layout_arithmetic():
 
 
 def test_varlen_host_check():
-    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5) == B.GDN_OK
-    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 1, 1, 4], 3, 4) == B.GDN_EINVAL
+    assert B.gdn_varlen_check_host(3, 200, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5) == B.GDN_OK
+    assert B.gdn_varlen_check_host(3, 200, [0, 65, 65, 200], [0, 1, 1, 4], 3, 4) == B.GDN_EINVAL
     assert "ceil(len/64)" in B.gdn_last_error()
-    assert B.gdn_varlen_check_host(3, [0, 65, 60, 200], [0, 2, 2, 5], 3, 5) == B.GDN_EINVAL
+    assert B.gdn_varlen_check_host(3, 200, [0, 65, 60, 200], [0, 2, 2, 5], 3, 5) == B.GDN_EINVAL
     assert "decreases" in B.gdn_last_error()
-    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 2, 5) == B.GDN_EINVAL
-    assert B.gdn_varlen_check_host(3, [0, 65, 65, 200], [0, 2, 2, 5], 3, 6) == B.GDN_EINVAL
+    assert B.gdn_varlen_check_host(3, 200, [0, 65, 65, 200], [0, 2, 2, 5], 2, 5) == B.GDN_EINVAL
+    assert B.gdn_varlen_check_host(3, 200, [0, 65, 65, 200], [0, 2, 2, 5], 3, 6) == B.GDN_EINVAL
+    # the offsets must end at the call's token count
+    assert B.gdn_varlen_check_host(3, 199, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5) == B.GDN_EINVAL
+    assert "cu_seqlens[B]=200 but T=199" in B.gdn_last_error()
+    assert B.gdn_varlen_check_host(3, 201, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5) == B.GDN_EINVAL
     # fewer than B + 1 offsets: refused before the library reads past them
     with pytest.raises(ValueError):
-        B.gdn_varlen_check_host(4, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5)
+        B.gdn_varlen_check_host(4, 200, [0, 65, 65, 200], [0, 2, 2, 5], 3, 5)
 
 
 def test_host_tensors_are_refused():
