@@ -239,6 +239,31 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
                 const gdn_strides *strides, const gdn_varlen *varlen, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): gdn_prefill_ex
+ * without a caller scratch buffer.  The call's intermediates (regions gc, tp
+ * and, with GDN_OPT_L2NORM_QK, nrm of the scratch layout) go to a fixed array of
+ * GDN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until
+ * the process ends; problems whose intermediates need more are rejected with
+ * GDN_ESCRATCH (128 MiB holds about 12 700 chunk slots: 64-token chunks times
+ * v-heads).  With GDN_OPT_ENTRY_STATES the entry states go to s_entry_out, the
+ * caller's output of slots x 128 x 128 bf16 (16-byte aligned; [slot][dv][dk]
+ * as region s_entry, slots numbered as in the scratch layout); without it
+ * s_entry_out is not read.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ * Every call on one GPU uses that GPU's one array and leaves its last contents
+ * there, so calls that overlap on a GPU (different streams or host threads)
+ * race: the caller serialises them.  The first call on a device looks the
+ * array's device address up, with that device current.  Arguments, checks and
+ * errors are otherwise those of gdn_prefill_ex.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdn_prefill_noalloc(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        void *h_state, int h_state_is_table, void *out, void *s_entry_out, int B, int T,
+                        int nk, int nv, int dk, int dv, const gdn_strides *strides,
+                        const gdn_varlen *varlen, unsigned flags, void *stream);
+
+/*
  * One kernel of gdn_prefill(_ex) (stage 1 or 2), same arguments, same
  * validation: the page runs its stages as sequential launches on one stream
  * (gdn_prefill_fla's doc comment), and so can a caller.  Stage 2 reads what

@@ -11,9 +11,17 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gdn_prefill.h"
 #include "gdn_params.h"
+
+// The scratch of gdn_prefill_noalloc (gc, T' and the row scales of one call):
+// a fixed array that every GPU the library runs on holds until the process
+// ends.  Host code never passes this name to a kernel -- in host code it is a
+// stand-in, not a device address; the device address comes from
+// hipGetSymbolAddress, looked up once per device (scratch_on below).
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
 
 namespace gdn {
 hipError_t launch_stage1(const Params &p, hipStream_t stream);
@@ -269,6 +277,34 @@ int run_stage(int stage, const gdn::Params &p, hipStream_t stream) {
   return ok();
 }
 
+// ---- the no-allocation variant ------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device dev: looked up with dev current, on
+// the first call for that device, then kept.
+int scratch_on(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_EHIP, "device %d: the no-allocation scratch is kept for devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(GDN_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(GDN_EHIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(GDN_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
 int validate_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
                     void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
                     const gdn_strides *strides) {
@@ -396,6 +432,42 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
                 const gdn_varlen *varlen, void *stream) {
   return gdn_prefill_ex(q, k, v, g, beta, h_state, h_state_is_table, out, scratch, scratch_bytes, B, T, nk, nv,
                         dk, dv, strides, varlen, GDN_OPT_ENTRY_STATES, stream);
+}
+
+int gdn_prefill_noalloc(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        void *h_state, int h_state_is_table, void *out, void *s_entry_out, int B, int T, int nk,
+                        int nv, int dk, int dv, const gdn_strides *strides, const gdn_varlen *varlen,
+                        unsigned flags, void *stream) {
+  int rc = validate_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, T, nk, nv, dk, dv, strides, varlen,
+                         flags);
+  if (rc != GDN_OK) return rc;
+  const bool entry = (flags & GDN_OPT_ENTRY_STATES) != 0;
+  if (entry && !s_entry_out)
+    return fail(GDN_EINVAL, "null pointer: s_entry_out is required with GDN_OPT_ENTRY_STATES");
+  if (entry && !aligned(s_entry_out, 16)) return fail(GDN_EINVAL, "alignment: s_entry_out must be 16-byte aligned");
+  // the intermediates only: the entry states are the caller's output
+  gdn_scratch_layout lay;
+  rc = layout(B, T, nk, nv, dk, dv, varlen, flags & ~unsigned(GDN_OPT_ENTRY_STATES), &lay);
+  if (rc != GDN_OK) return rc;
+  if (lay.total > GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ESCRATCH,
+                "no-allocation scratch: %lld chunk slots need %zu bytes of intermediates, the fixed array holds "
+                "%zu; use gdn_prefill_ex with a caller scratch for problems this large",
+                (long long)lay.slots, lay.total, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  int dev = -1;
+  const hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDN_EHIP, "device of the stream: %s", hipGetErrorString(e));
+  void *base = nullptr;
+  rc = scratch_on(dev, &base);
+  if (rc != GDN_OK) return rc;
+  gdn::Params p = make_params(q, k, v, g, beta, h_state, h_state_is_table, out, base, B, T, nk, nv, strides,
+                              varlen, lay, entry ? s_entry_out : nullptr);
+  p.opts = flags;
+  for (int stage = 1; stage <= 2; ++stage) {
+    rc = run_stage(stage, p, static_cast<hipStream_t>(stream));
+    if (rc != GDN_OK) return rc;
+  }
+  return GDN_OK;
 }
 
 int gdn_varlen_check_host(int B, int T, const int32_t *cu_seqlens_host, const int32_t *cu_chunks_host,
