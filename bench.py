@@ -113,6 +113,20 @@ def algorithmic(p, flags=OPT_ENTRY_STATES):
     return by, fl
 
 
+def read_write_bytes(p, flags):
+    """Per kernel, the (read, write) split of algorithmic()'s bytes."""
+    N, nk, nv = p.n_tokens, p.nk, p.nv
+    slots = int(p.cu_chunks[-1]) * nv
+    d, C = 128, 64
+    norm = bool(flags & OPT_L2NORM_QK)
+    qk = N * nk * d * 2
+    small = slots * C * 4 + slots * 2 * 2560 * 2 + (slots * 2 * C * 4 if norm else 0)  # gc, T', row scales
+    state = p.nseq * nv * d * d * 4
+    s_out = slots * d * d * 2 if flags & OPT_ENTRY_STATES else 0
+    return {1: (qk * (2 if norm else 1) + N * nv * 8, small),
+            2: (2 * qk + N * nv * d * 2 + small + state, N * nv * d * 2 + s_out + state)}
+
+
 def workload_flags(meta, raw_qk=False, entry_states="auto"):
     """Call options for a workload: entry states where it asks for them (or as
     ``entry_states`` = "on" / "off" forces), q/k normalisation in the kernels
@@ -407,6 +421,71 @@ def section_stamps(args):
     print(json.dumps(out), flush=True)
 
 
+def workload_shape(index):
+    """The sizes the byte models read, without drawing the workload's values:
+    token count, heads, sequence count and chunk offsets."""
+    from types import SimpleNamespace
+    import numpy as np
+    from linear_attention_ssm_chunk_amd import inputs as I
+    w = I.WORKLOADS[index]
+    lengths = I.ragged_lengths(index, w["nseq"])[0] if "nseq" in w else [w["T"]] * w["B"]
+    cu_chunks = np.concatenate([[0], np.cumsum([-(-L // 64) for L in lengths])])
+    return SimpleNamespace(n_tokens=int(sum(lengths)), nk=w["nk"], nv=w["nv"], nseq=len(lengths),
+                           cu_chunks=cu_chunks, meta=dict(w))
+
+
+def stream_ceiling(args):
+    """The achievable HBM rate for each kernel's read:write mix on this GPU:
+    a streaming kernel (profiling build) reads and writes the same byte counts
+    as the kernel does on the workload, interleaved in the same ratio; best of
+    three grid sizes, 20 timed launches each after warm-up."""
+    import ctypes
+    import torch
+    from linear_attention_ssm_chunk_amd import binding, build
+    L = binding.load(build.LIB_STAMPS)
+    L.gdn_debug_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.gdn_debug_stream_mix.restype = ctypes.c_int
+    p = workload_shape(args.workload)
+    flags = workload_flags(p.meta, args.raw_qk, args.entry_states)
+    rw = read_write_bytes(p, flags)
+    mixes = {KERNELS[st]: rw[st] for st in sorted(rw)}
+    mixes["whole step"] = (rw[1][0] + rw[2][0], rw[1][1] + rw[2][1])
+    mixes["copy 1:1"] = (max(rw[2]), max(rw[2]))
+    biggest = max(max(r, w) for r, w in mixes.values())
+    src = torch.zeros(biggest // 4 + 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty(biggest // 4 + 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"workload": p.meta["name"], "entry_states": bool(flags & OPT_ENTRY_STATES), "mixes": {}}
+    for name, (r, w) in mixes.items():
+        r, w = r // 16 * 16, w // 16 * 16
+        best = None
+        for blocks in (1024, 2048, 4096):
+            def launch():
+                rc = L.gdn_debug_stream_mix(src.data_ptr(), r, dst.data_ptr(), w, sink.data_ptr(), blocks, stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream_mix failed ({rc})")
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < WARMUP_MIN_S:
+                launch()
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            gbs = (r + w) / (ms / 1e3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, blocks, ms)
+        out["mixes"][name] = {"read_bytes": r, "write_bytes": w, "read_share": round(r / (r + w), 3),
+                              "GBps": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4),
+                              "blocks": best[1], "ms": round(best[2], 4)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -422,6 +501,8 @@ def main():
                     help="measure the recurrent decode step (gdn_decode) on a batch of 256 sequences instead")
     ap.add_argument("--section-stamps", action="store_true",
                     help="cycles per section of the spine's step from the profiling build (not a timing run)")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="the achievable HBM rate of each kernel's read:write mix (profiling build's streaming kernel)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (three times), to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -458,6 +539,9 @@ def main():
         return
     if args.section_stamps:
         section_stamps(args)
+        return
+    if args.stream_ceiling:
+        stream_ceiling(args)
         return
 
     from linear_attention_ssm_chunk_amd import inputs as I

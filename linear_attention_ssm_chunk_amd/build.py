@@ -4,8 +4,9 @@
     python -m linear_attention_ssm_chunk_amd.build --stamps   # and its section-stamp profiling build
 
 The profiling build (libgdn_prefill_stamps.so, -DGDN_SECTION_STAMPS) is the same
-sources with clock stamps at the spine's section marks; bench.py
---section-stamps loads it.  Nothing else loads it.
+sources with clock stamps at the spine's section marks, plus the streaming
+kernel of stream_mix.hip; bench.py --section-stamps and --stream-ceiling load
+it.  Nothing else loads it.
 
 Every HIP source is compiled with packed FP32 math disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns
@@ -45,6 +46,8 @@ def build(verbose=False, stamps=False):
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     lib = LIB_STAMPS if stamps else LIB
     tmp = lib + ".tmp"
+    if stamps:  # the measurement-only streaming kernel rides along in the profiling build
+        srcs.append(os.path.join(CSRC, "stream_mix.hip"))
     cmd = [hipcc()] + FLAGS + (["-DGDN_SECTION_STAMPS"] if stamps else []) + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -159,8 +159,20 @@ __device__ __forceinline__ void split_tiles(const f32x4 &t0, const f32x4 &t1, ui
   lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
+// Loader waves per workgroup: four, and six where the output moves onto the
+// loaders (S <= 2, below).
+template <int kStrips> constexpr int loader_waves() { return kStrips <= 2 ? 6 : 4; }
+
 template <int kStrips, bool kEntry>
-__global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params p) {
+__global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chunk_delta_h_fwd_o(Params p) {
+  // With S <= 2 strips per workgroup two SIMDs hold no compute wave and the
+  // LDS has room, so the output moves off the compute waves (kOL): the loader
+  // that formed chunk c's scores in step c keeps them, chunk c's Q fragments
+  // and its output decays in registers, and in step c+1 reads the compute
+  // waves' bf16 h and bf16 uc of chunk c from LDS (tiles ht, ut, written in
+  // step c) and forms O^T = diag(exp(G)) (h^T Q^T) + uc^T A^T itself.  The Q
+  // and K rows are then fetched by two waves per pair instead of one.
+  constexpr bool kOL = kStrips <= 2;
   constexpr int kGroups = 8 / kStrips; // workgroups per chain
   // ---- which (sequence, v-head, column group) ----------------------------
   const int r = p.nv / p.nk;
@@ -175,14 +187,22 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   if (!s.ok || s.nchunks == 0) return; // length 0: the state is left as it is
   const int nch = s.nchunks;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is made scalar, so that branches on a wave's role are
+  // scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, r16 = lane & 15;
   const int col0 = cg * 16 * kStrips; // first column of this workgroup
 
   __shared__ Stage st[2];
   // scores A of chunk c (A operand of A uc, fragment tri_frag(mt, kb)) in
-  // afb[c % 2]: formed in step c, used in step c+1
-  __shared__ u32x4 afb[2][kTpFrags * 64];
+  // afb[c % 2]: formed in step c, used in step c+1 (S = 4; with kOL they stay
+  // in the registers of the loader that formed them)
+  __shared__ u32x4 afb[2][kOL ? 1 : kTpFrags * 64];
+  // kOL: bf16 h and bf16 uc of chunk c per compute wave, its fragments Hh[kb]
+  // and ub[kb] as 64 lanes x 16 bytes each, in ht / ut [c % 2][wave]: written
+  // in step c, read in step c+1, written again in step c+2
+  __shared__ u32x4 ht[kOL ? 2 * kStrips * 4 * 64 : 1];
+  __shared__ u32x4 ut[kOL ? 2 * kStrips * 2 * 64 : 1];
   // Output tiles, [token][workgroup column] bf16 with a row pitch of
   // 32 * kStrips + 16 bytes (16 rows of one column block fall in distinct
   // banks): chunk c's tile ost[c % 2] is written in step c+1 and stored in
@@ -194,11 +214,14 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
   if (wave >= kStrips) {
     // Loader li = wave - S belongs to pair li % 2.  Waves are dealt to the four
     // SIMDs in turn, so for S <= 2 loaders li = 0, 1 sit on SIMDs without a
-    // compute wave: they take role 1 (with the score products), and the light
-    // role 0 shares a SIMD with a compute wave.  For S = 4 every SIMD holds one
-    // compute wave and one loader.
-    const int pair = (wave - kStrips) & 1; // stages chunks c with c % 2 == pair
-    const int role = (kStrips <= 2) ? 1 - ((wave - kStrips) >> 1) : ((wave - kStrips) >> 1);
+    // compute wave: they take role 1 (T', V, gate sums; the score products and,
+    // with kOL, the output); role 0 (Q rows, and the K rows for S = 4; the
+    // output stores) shares a SIMD with a compute wave; with kOL role 2 (the K
+    // rows) sits beside a role-1 wave.  For S = 4 every SIMD holds one compute
+    // wave and one loader.
+    const int li = wave - kStrips;
+    const int pair = li & 1; // stages chunks c with c % 2 == pair
+    const int role = kOL ? ((li >> 1) == 0 ? 1 : (li >> 1) == 1 ? 0 : 2) : (li >> 1);
     const int nrow = lane >> 4, piece = lane & 15; // whole-row loads: 4 rows per instruction
     // rows of the workgroup's 16 * kStrips columns: 2 * kStrips pieces per row
     constexpr int kVPieces = 2 * kStrips, kVRows = 64 / kVPieces;
@@ -208,16 +231,17 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     // (A = K rows s, B = Q rows t; lane holds column t = 16mt + r16, rows
     // s = 16ms + 4q .. +3), masked to s <= t and decayed by exp(G_t - G_s)
     // (times sq_t sk_s with q/k normalisation);
-    // two vertically stacked tiles are the chain-order A fragment (mt, kb).
+    // two vertically stacked tiles are the chain-order A fragment (mt, kb),
+    // left in A[tri_frag(mt, kb)]; the Q row fragments are left in qf.
     // Only the fragments of the row blocks mt in the bit mask are formed (the
     // caller passes Mask<bits>).
-    auto scores = [&](const Stage &S, u32x4 *A, auto mask_tag) __attribute__((always_inline)) {
+    auto scores = [&](const Stage &S, u32x4 (&A)[kTpFrags], bf16x8 (&qf)[16], auto mask_tag)
+                      __attribute__((always_inline)) {
       constexpr int mask = decltype(mask_tag)::value;
       constexpr int top = (mask & 8) ? 3 : (mask & 4) ? 2 : (mask & 2) ? 1 : 0;
       auto frag = [&](const u32x4 *T, int mt, int kb) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8, T[row_slot(16 * mt + r16, 4 * kb + q4)]);
       };
-      bf16x8 qf[16];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -256,37 +280,56 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         for (int kb = 0; kb < 2; ++kb) {
           if (2 * kb > mt) continue;
           const f32x4 hi_tile = (2 * kb + 1 <= mt) ? sc[mt][2 * kb + 1] : zero4();
-          A[tri_frag(mt, kb) * 64 + lane] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
+          A[tri_frag(mt, kb)] = __builtin_bit_cast(u32x4, chain_frag(sc[mt][2 * kb], hi_tile));
         }
       }
     };
+    // S = 4: the fragments of the row blocks in the mask go to afb for the
+    // compute waves
+    auto scores_to_lds = [&](const Stage &S, u32x4 *dst, auto mask_tag) __attribute__((always_inline)) {
+      constexpr int mask = decltype(mask_tag)::value;
+      u32x4 A[kTpFrags];
+      bf16x8 qf[16];
+      scores(S, A, qf, mask_tag);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if ((mask & (1 << mt)) && 2 * kb <= mt) dst[tri_frag(mt, kb) * 64 + lane] = A[tri_frag(mt, kb)];
+    };
     GDN_STAMP_DECL;
-    if (role == 0) {
+    if (role != 1) {
       // ---- Q, K rows; outputs --------------------------------------------
-      u32x4 qx[16], kx[16]; // qx[j] = Q[4j + lane/16][8 (lane%16) .. +7]
+      // (with kOL role 0 takes the Q rows and the outputs, role 2 the K rows)
+      // with kOL roles 0 and 2 move one operand each (Q rows, K rows) through
+      // the same registers, chosen by a wave-uniform pointer rather than a
+      // branch per load (a load under a branch waits for every load before it)
+      constexpr int kOps = kOL ? 1 : 2;
+      const bool doQ = !kOL || role == 0;
+      u32x4 rx[kOps][16]; // rx[o][j] = operand row 4j + lane/16, bf16 8 (lane%16) .. +7
       auto fetch = [&](int c) __attribute__((always_inline)) {
         const int nn = min(kChunk, s.len - c * kChunk);
         // chunk bases are wave-uniform; a lane adds a 32-bit offset (row
         // pitches are bounded so that 64 rows stay below 2^31 bytes)
         const int64_t row0 = (s.tok0 + int64_t(c) * kChunk) * p.qk_row + int64_t(kh) * kDim;
-        const char *qc = reinterpret_cast<const char *>(p.q + row0);
-        const char *kc = reinterpret_cast<const char *>(p.k + row0);
+        const char *src[2] = {reinterpret_cast<const char *>((doQ ? p.q : p.k) + row0),
+                              reinterpret_cast<const char *>(p.k + row0)};
         const uint32_t pitch = uint32_t(p.qk_row) * 2u;
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
           // rows past the sequence end repeat its last row: they only reach
           // rows of products that are never stored, or meet zero rows of T'
           const uint32_t off = uint32_t(min(4 * jr + nrow, nn - 1)) * pitch + 16u * piece;
-          qx[jr] = *reinterpret_cast<const u32x4 *>(qc + off);
-          kx[jr] = *reinterpret_cast<const u32x4 *>(kc + off);
+#pragma unroll
+          for (int o = 0; o < kOps; ++o) rx[o][jr] = *reinterpret_cast<const u32x4 *>(src[o] + off);
         }
       };
       auto stash = [&](Stage &S) __attribute__((always_inline)) {
+        u32x4 *dst[2] = {doQ ? S.qr : S.kr, S.kr};
 #pragma unroll
-        for (int jr = 0; jr < 16; ++jr) {
-          S.qr[row_slot(4 * jr + nrow, piece)] = qx[jr];
-          S.kr[row_slot(4 * jr + nrow, piece)] = kx[jr];
-        }
+        for (int jr = 0; jr < 16; ++jr)
+#pragma unroll
+          for (int o = 0; o < kOps; ++o) dst[o][row_slot(4 * jr + nrow, piece)] = rx[o][jr];
       };
       // outputs of chunk co (tile co % 2): whole row segments of the
       // workgroup's columns
@@ -318,15 +361,16 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         }
         // the idle pair stores the output of chunk c-2 and, for S = 4, forms
         // half of chunk c's scores
-        if ((c & 1) == pair && c >= 2) store_out(c - 2);
-        if (kStrips == 4 && (c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<0x9>());
+        if (doQ && (c & 1) == pair && c >= 2) store_out(c - 2);
+        if constexpr (kStrips == 4)
+          if ((c & 1) == pair && c < nch) scores_to_lds(st[c & 1], afb[c & 1], Mask<0x9>());
         GDN_STAMP(3);
         __syncthreads();
         GDN_STAMP(4);
         GDN_STAMP_FLUSH(c);
       }
       // after the last barrier: the last chunk's output
-      if ((nch & 1) == pair) store_out(nch - 1);
+      if (doQ && (nch & 1) == pair) store_out(nch - 1);
       return;
     }
 
@@ -381,6 +425,42 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
       for (int jj = 0; jj < kVPieces; ++jj) S.vr[vrow_slot(vrow0 + jj * kVRows, vpiece)] = vx[jj];
     };
+    // kOL: chunk co's scores, Q fragments and output decays, kept from the
+    // step that formed the scores (co) to the next, which forms its output
+    u32x4 a_keep[kTpFrags];
+    bf16x8 q_keep[16];
+    float dq_keep[4];
+    // kOL: the output of chunk co for the workgroup's strips, into its output
+    // tile ost[co % 2]: O^T = diag(dq) (h^T Q^T) + uc^T A^T per strip, with
+    // bf16 h and bf16 uc read from ht / ut
+    auto output = [&](int co) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < kStrips; ++w) {
+        const u32x4 *hti = ht + ((co & 1) * kStrips + w) * 4 * 64 + lane;
+        const u32x4 *uti = ut + ((co & 1) * kStrips + w) * 2 * 64 + lane;
+        f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 hb = __builtin_bit_cast(bf16x8, hti[kb * 64]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(hb, q_keep[4 * mt + kb], O[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) O[mt] *= dq_keep[mt];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ub = __builtin_bit_cast(bf16x8, uti[kb * 64]);
+#pragma unroll
+          for (int mt = 2 * kb; mt < 4; ++mt)
+            O[mt] = mfma(ub, __builtin_bit_cast(bf16x8, a_keep[tri_frag(mt, kb)]), O[mt]);
+        }
+        char *ot = &ost[co & 1][32 * w + 8 * q4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          *reinterpret_cast<u32x2 *>(ot + (16 * mt + r16) * kOPitch) =
+              pack4_bf16(O[mt][0], O[mt][1], O[mt][2], O[mt][3]);
+      }
+    };
     if (pair < nch) fetch(pair);
     if (pair == 0) {
       stash(st[0]);
@@ -396,8 +476,19 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
         if (c + 3 < nch) fetch(c + 3);
         GDN_STAMP(2);
       }
-      // the idle pair forms the scores of chunk c (with role 0 for S = 4)
-      if ((c & 1) == pair && c < nch) scores(st[c & 1], afb[c & 1], Mask<kStrips == 4 ? 0x6 : 0xF>());
+      if constexpr (kOL) {
+        // the active pair forms the output of chunk c-1, whose scores it
+        // formed in step c-1; the idle pair forms (and keeps) chunk c's
+        if (((c + 1) & 1) == pair && c >= 1) output(c - 1);
+        if ((c & 1) == pair && c < nch) {
+          scores(st[c & 1], a_keep, q_keep, Mask<0xF>());
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) dq_keep[mt] = st[c & 1].dq[16 * mt + r16];
+        }
+      } else {
+        // the idle pair forms the scores of chunk c (with role 0 for S = 4)
+        if ((c & 1) == pair && c < nch) scores_to_lds(st[c & 1], afb[c & 1], Mask<0x6>());
+      }
       GDN_STAMP(3);
       __syncthreads();
       GDN_STAMP(4);
@@ -485,78 +576,125 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     // colw + r16, so they leave as 16-byte pieces of the [dv][dk] rows
     uint16_t *edst = kEntry ? p.s_entry + sl * (kDim * kDim) + (colw + r16) * kDim + 8 * q4 : nullptr;
 
-    // ---- h -> hi/lo (chain order over dk, eight consecutive dk per lane);
-    // bf16(h) is the entry state.  The previous chunk's output, then Q h, the
-    // output's state term, issue among the split's vector instructions.
     bf16x8 Hh[4], Hl[4];
-    bf16x8 kA[4][2], qa[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) kA[kb][mt] = rfrag(S.kr, mt, kb);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) qa[0][mt] = rfrag(S.qr, mt, 0);
-    const float en = S.en[0]; // exp(G_n)
-    if (c > 0) {
-      bf16x8 af[kTpFrags];
-      load_scores(c - 1, af);
-      finish_output(c - 1, af);
-    }
-    // exp(G_n) h goes to new registers before each pair is split, so that the
-    // split can overwrite h in place
     f32x4 Hn[8];
-    Hn[0] = H[0] * en;
-    Hn[1] = H[1] * en;
-    split_tiles(H[0], H[1], m0, m1, Hh[0], Hl[0]);
-    if (kEntry) *reinterpret_cast<u32x4 *>(edst) = __builtin_bit_cast(u32x4, Hh[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    GDN_STAMP(1);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) O[mt] = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (kb < 3) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) qa[(kb + 1) & 1][mt] = rfrag(S.qr, mt, kb + 1);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(Hh[kb], qa[kb & 1][mt], O[mt]);
-      if (kb < 3) {
-        Hn[2 * kb + 2] = H[2 * kb + 2] * en;
-        Hn[2 * kb + 3] = H[2 * kb + 3] * en;
-        split_tiles(H[2 * kb + 2], H[2 * kb + 3], m0, m1, Hh[kb + 1], Hl[kb + 1]);
-        if (kEntry) *reinterpret_cast<u32x4 *>(edst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
-        GDN_INTERLEAVE(4, 5, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    GDN_STAMP(2);
-
-    // ---- K h, half A (rows 0..31), while h is scaled by exp(G_n) ----------
     bf16x8 kB[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) kB[kb][mt] = rfrag(S.kr, mt + 2, kb);
     f32x4 eg[4];
     u32x2 vv[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      eg[mt] = *reinterpret_cast<const f32x4 *>(S.eg + 16 * mt + 4 * q4);
-      // V[16mt + 4q + ii][colw + r16], ii = 0..3: a transposing read of the V rows
-      vv[mt] = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
-    }
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    // the operands of K h rows 32..63 and of R, issued during the split
+    auto load_kb_eg_v = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        acc[mt] = mfma(kA[kb][mt], Hh[kb], acc[mt]);
-        acc[mt] = mfma(kA[kb][mt], Hl[kb], acc[mt]);
+        for (int mt = 0; mt < 2; ++mt) kB[kb][mt] = rfrag(S.kr, mt + 2, kb);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        eg[mt] = *reinterpret_cast<const f32x4 *>(S.eg + 16 * mt + 4 * q4);
+        // V[16mt + 4q + ii][colw + r16], ii = 0..3: a transposing read of the V rows
+        vv[mt] = read_tr(S.vr, vrow_slot(16 * mt + 4 * q4 + (r16 >> 2), 2 * wave + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1));
       }
-    GDN_INTERLEAVE(16, 2, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    GDN_STAMP(3);
+    };
+    if constexpr (kOL) {
+      // ---- h -> hi/lo (chain order over dk, eight consecutive dk per lane),
+      // each pair's bf16 h to ht (the output's h) and, when asked for, out as
+      // the entry state; K h rows 0..31 of each pair's dk block issue while
+      // the next pair is split
+      u32x4 *hto = ht + ((c & 1) * kStrips + wave) * 4 * 64 + lane;
+      bf16x8 kA[4][2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) kA[kb][mt] = rfrag(S.kr, mt, kb);
+      const float en = S.en[0]; // exp(G_n)
+      // exp(G_n) h goes to new registers before each pair is split, so that the
+      // split can overwrite h in place
+      Hn[0] = H[0] * en;
+      Hn[1] = H[1] * en;
+      split_tiles(H[0], H[1], m0, m1, Hh[0], Hl[0]);
+      hto[0] = __builtin_bit_cast(u32x4, Hh[0]);
+      if (kEntry) *reinterpret_cast<u32x4 *>(edst) = __builtin_bit_cast(u32x4, Hh[0]);
+      load_kb_eg_v();
+      __builtin_amdgcn_sched_barrier(0);
+      GDN_STAMP(1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          acc[mt] = mfma(kA[kb][mt], Hh[kb], acc[mt]);
+          acc[mt] = mfma(kA[kb][mt], Hl[kb], acc[mt]);
+        }
+        if (kb < 3) {
+          Hn[2 * kb + 2] = H[2 * kb + 2] * en;
+          Hn[2 * kb + 3] = H[2 * kb + 3] * en;
+          split_tiles(H[2 * kb + 2], H[2 * kb + 3], m0, m1, Hh[kb + 1], Hl[kb + 1]);
+          hto[64 * (kb + 1)] = __builtin_bit_cast(u32x4, Hh[kb + 1]);
+          if (kEntry) *reinterpret_cast<u32x4 *>(edst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
+          GDN_INTERLEAVE(4, 6, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      GDN_STAMP(2);
+      GDN_STAMP(3);
+    } else {
+      // ---- h -> hi/lo (chain order over dk, eight consecutive dk per lane);
+      // bf16(h) is the entry state.  The previous chunk's output, then Q h, the
+      // output's state term, issue among the split's vector instructions.
+      bf16x8 kA[4][2], qa[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) kA[kb][mt] = rfrag(S.kr, mt, kb);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) qa[0][mt] = rfrag(S.qr, mt, 0);
+      const float en = S.en[0]; // exp(G_n)
+      if (c > 0) {
+        bf16x8 af[kTpFrags];
+        load_scores(c - 1, af);
+        finish_output(c - 1, af);
+      }
+      // exp(G_n) h goes to new registers before each pair is split, so that the
+      // split can overwrite h in place
+      Hn[0] = H[0] * en;
+      Hn[1] = H[1] * en;
+      split_tiles(H[0], H[1], m0, m1, Hh[0], Hl[0]);
+      if (kEntry) *reinterpret_cast<u32x4 *>(edst) = __builtin_bit_cast(u32x4, Hh[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      GDN_STAMP(1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) O[mt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb < 3) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) qa[(kb + 1) & 1][mt] = rfrag(S.qr, mt, kb + 1);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) O[mt] = mfma(Hh[kb], qa[kb & 1][mt], O[mt]);
+        if (kb < 3) {
+          Hn[2 * kb + 2] = H[2 * kb + 2] * en;
+          Hn[2 * kb + 3] = H[2 * kb + 3] * en;
+          split_tiles(H[2 * kb + 2], H[2 * kb + 3], m0, m1, Hh[kb + 1], Hl[kb + 1]);
+          if (kEntry) *reinterpret_cast<u32x4 *>(edst + 32 * (kb + 1)) = __builtin_bit_cast(u32x4, Hh[kb + 1]);
+          GDN_INTERLEAVE(4, 5, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      GDN_STAMP(2);
+
+      // ---- K h, half A (rows 0..31), while h is scaled by exp(G_n) ----------
+      load_kb_eg_v();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          acc[mt] = mfma(kA[kb][mt], Hh[kb], acc[mt]);
+          acc[mt] = mfma(kA[kb][mt], Hl[kb], acc[mt]);
+        }
+      GDN_INTERLEAVE(16, 2, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      GDN_STAMP(3);
+    }
 
     // ---- K h, half B, while R = V - diag(exp(G)) K h of half A is formed ---
     bf16x8 th[kTpFrags], tl[kTpFrags];
@@ -603,7 +741,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       dn[mt] = *reinterpret_cast<const f32x4 *>(S.dn + 16 * mt + 4 * q4);
-      dq[mt] = S.dq[16 * mt + r16];
+      if constexpr (!kOL) dq[mt] = S.dq[16 * mt + r16];
     }
     f32x4 D[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -632,11 +770,14 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     }
     bf16x8 Dh[2], Dl[2];
     ub[0] = chain_frag(D[0], D[1]);
+    if constexpr (kOL) ut[((c & 1) * kStrips + wave) * 2 * 64 + lane] = __builtin_bit_cast(u32x4, ub[0]);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) D[mt] *= dn[mt];
     split_tiles(D[0], D[1], m0, m1, Dh[0], Dl[0]);
+    if constexpr (!kOL) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) O[mt] *= dq[mt];
+      for (int mt = 0; mt < 4; ++mt) O[mt] *= dq[mt];
+    }
     GDN_INTERLEAVE(6, 6, 4);
     __builtin_amdgcn_sched_barrier(0);
     GDN_STAMP(6);
@@ -652,6 +793,7 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
       Hn[m] = mfma(kt0[m], Dl[0], Hn[m]);
     }
     ub[1] = chain_frag(D[2], D[3]);
+    if constexpr (kOL) ut[((c & 1) * kStrips + wave) * 2 * 64 + 64 + lane] = __builtin_bit_cast(u32x4, ub[1]);
 #pragma unroll
     for (int mt = 2; mt < 4; ++mt) D[mt] *= dn[mt];
     split_tiles(D[2], D[3], m0, m1, Dh[1], Dl[1]);
@@ -673,8 +815,9 @@ __global__ __launch_bounds__((kStrips + 4) * 64) void chunk_delta_h_fwd_o(Params
     GDN_STAMP(9);
     GDN_STAMP_FLUSH(c);
   }
-  // the last chunk's output: its scores were formed in the last step
-  {
+  // the last chunk's output: its scores were formed in the last step (kOL:
+  // a loader forms it in the step this barrier closes)
+  if constexpr (!kOL) {
     bf16x8 af[kTpFrags];
     load_scores(nch - 1, af);
     finish_output(nch - 1, af);
@@ -705,10 +848,11 @@ hipError_t launch_with(const Params &p, hipStream_t stream) {
   const int r = p.nv / p.nk;
   const int kgroups = p.B * p.nk;
   const int blocks = 8 * ((kgroups + 7) / 8) * r * (8 / kStrips);
+  const dim3 block((kStrips + loader_waves<kStrips>()) * 64);
   if (p.opts & kOptEntry)
-    hipLaunchKernelGGL((chunk_delta_h_fwd_o<kStrips, true>), dim3(blocks), dim3((kStrips + 4) * 64), 0, stream, p);
+    hipLaunchKernelGGL((chunk_delta_h_fwd_o<kStrips, true>), dim3(blocks), block, 0, stream, p);
   else
-    hipLaunchKernelGGL((chunk_delta_h_fwd_o<kStrips, false>), dim3(blocks), dim3((kStrips + 4) * 64), 0, stream, p);
+    hipLaunchKernelGGL((chunk_delta_h_fwd_o<kStrips, false>), dim3(blocks), block, 0, stream, p);
   return hipGetLastError();
 }
 } // namespace

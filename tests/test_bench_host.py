@@ -8,8 +8,6 @@ import json
 import os
 import subprocess
 import sys
-from types import SimpleNamespace
-
 import numpy as np
 import pytest
 
@@ -22,15 +20,8 @@ from linear_attention_ssm_chunk_amd import inputs as I  # noqa: E402
 
 def shape_of(index):
     """The sizes bench.algorithmic reads, without drawing the workload's
-    values: token count, heads and chunk offsets."""
-    w = I.WORKLOADS[index]
-    if "nseq" in w:
-        lengths, _ = I.ragged_lengths(index, w["nseq"])
-    else:
-        lengths = [w["T"]] * w["B"]
-    cu_chunks = np.concatenate([[0], np.cumsum([-(-L // 64) for L in lengths])])
-    return SimpleNamespace(n_tokens=int(sum(lengths)), nk=w["nk"], nv=w["nv"], nseq=len(lengths),
-                           cu_chunks=cu_chunks)
+    values (bench.workload_shape)."""
+    return bench.workload_shape(index)
 
 
 def test_shape_of_matches_the_drawn_workload():
