@@ -341,18 +341,38 @@ def traffic_for_decode():
 
 STAMP_FIRST, STAMP_STEPS, STAMP_SLOTS, STAMP_WAVES = 8, 32, 16, 8  # gdn_params.h
 COMPUTE_SECTIONS = {  # mark k closes the section that began at mark k-1 (k2_chunk_delta_h_fwd_o.hip)
-    1: "split h (first pair), entry-state tile write, previous chunk's A uc and output tile",
-    2: "Q h (output state term) with the rest of the split",
-    3: "K h rows 0..31 (entry states 0..63 out)",
-    4: "K h rows 32..63, R rows 0..31 (entry states 64..127 out)",
-    5: "T' R rows 0..31 and R rows 32..63",
-    6: "T' R rows 32..63; uc rows 0..31 decayed and split",
-    7: "K^T uc rows 0..31; uc rows 32..63 decayed and split",
-    8: "K^T uc rows 32..63",
-    9: "barrier wait",
+    4: {  # four strips per workgroup: the compute waves form the output
+        1: "split h (first pair), entry-state tile write, previous chunk's A uc and output tile",
+        2: "Q h (output state term) with the rest of the split",
+        3: "K h rows 0..31 (entry states 0..63 out)",
+        4: "K h rows 32..63, R rows 0..31 (entry states 64..127 out)",
+        5: "T' R rows 0..31 and R rows 32..63",
+        6: "T' R rows 32..63; uc rows 0..31 decayed and split",
+        7: "K^T uc rows 0..31; uc rows 32..63 decayed and split",
+        8: "K^T uc rows 32..63",
+        9: "barrier wait",
+    },
+    2: {  # one or two strips: the output is formed on a loader
+        1: "split h (first pair), bf16 h and entry-state tile writes, operand reads",
+        2: "K h rows 0..31 with the rest of the split",
+        3: "(no section)",
+        4: "K h rows 32..63, R rows 0..31",
+        5: "T' R rows 0..31 and R rows 32..63",
+        6: "T' R rows 32..63; uc rows 0..31 to the output tile, decayed and split",
+        7: "K^T uc rows 0..31; uc rows 32..63 to the output tile, decayed and split",
+        8: "K^T uc rows 32..63",
+        9: "barrier wait",
+    },
 }
-LOADER_SECTIONS = {1: "stage chunk c+1 into LDS (active pair)", 2: "issue fetch of chunk c+3 (active pair)",
-                   3: "scores / output stores (idle pair)", 4: "barrier wait"}
+# loader roles: (name, what marks 1, 2, 3 close in a step where the pair stages
+# the next chunk ("active"), what mark 3 closes in the other steps ("idle"))
+LOADER_ROLES = {
+    (4, 0): ("Q and K rows; output stores; score rows 0 and 3", "stage", "issue fetch", "-", "output stores, scores"),
+    (4, 1): ("T', V, gate factors; score rows 1 and 2", "stage", "issue fetch", "-", "scores"),
+    (2, 0): ("Q rows; output stores", "delay and stage", "issue fetch", "-", "delay and output stores"),
+    (2, 1): ("T', V, gate factors; scores; output", "stage", "issue fetch", "output", "scores"),
+    (2, 2): ("K rows", "delay and stage", "issue fetch", "-", "delay"),
+}
 
 
 def section_stamps(args):
@@ -395,23 +415,24 @@ def section_stamps(args):
     step_cyc = np.diff(w0[:steps + 1, 0])
     step_rt = np.diff(w0[:steps + 1, 15])  # 100 MHz ticks
     clock = float(step_cyc.sum() / step_rt.sum() * 0.1)  # GHz
-    comp = {COMPUTE_SECTIONS[k]: round(float(np.mean(w0[:steps, k] - w0[:steps, k - 1])), 1) for k in range(1, 10)}
+    names = COMPUTE_SECTIONS[4 if strips == 4 else 2]
+    comp = {names[k]: round(float(np.mean(w0[:steps, k] - w0[:steps, k - 1])), 1) for k in range(1, 10)}
     loaders = {}
-    for w in range(strips, strips + 4):
+    nload = 4 if strips == 4 else 6
+    for w in range(strips, min(strips + nload, STAMP_WAVES)):
         li = w - strips
-        role = (1 - (li >> 1)) if strips <= 2 else (li >> 1)
+        role = (li >> 1) if strips == 4 else (1, 0, 2)[li >> 1]
+        name, m1, m2, m3, idle3 = LOADER_ROLES[(4 if strips == 4 else 2, role)]
         pair = li & 1
         t = st[w].astype(np.float64)
         # a loader stages in step c when (c + 1) % 2 == pair and is idle otherwise
         act = [c for c in range(steps) if (STAMP_FIRST + c + 1) % 2 == pair]
         idle = [c for c in range(steps) if (STAMP_FIRST + c) % 2 == pair]
         mean = lambda cs, k1, k0: round(float(np.mean([t[c, k1] - t[c, k0] for c in cs])), 1)  # noqa: E731
-        loaders[f"wave {w} (role {role})"] = {
-            "active step: " + LOADER_SECTIONS[1]: mean(act, 1, 0),
-            "active step: " + LOADER_SECTIONS[2]: mean(act, 2, 1),
-            "active step: " + LOADER_SECTIONS[4]: mean(act, 4, 3),
-            "idle step: " + LOADER_SECTIONS[3]: mean(idle, 3, 0),
-            "idle step: " + LOADER_SECTIONS[4]: mean(idle, 4, 3)}
+        loaders[f"wave {w}: {name}"] = {
+            "active: " + m1: mean(act, 1, 0), "active: " + m2: mean(act, 2, 1), "active: " + m3: mean(act, 3, 2),
+            "active: barrier wait": mean(act, 4, 3),
+            "idle: " + idle3: mean(idle, 3, 0), "idle: barrier wait": mean(idle, 4, 3)}
     out = {"workload": p.meta["name"], "entry_states": bool(flags & OPT_ENTRY_STATES),
            "strips_per_workgroup": strips, "chunks": nch,
            "stamped_steps": f"{STAMP_FIRST}..{STAMP_FIRST + steps - 1} of sequence 0, v-head 0, workgroup 0",
