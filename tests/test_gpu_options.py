@@ -109,6 +109,30 @@ def test_l2norm_single_stream_every_chain(dev):
     assert_within(wc, intermediates=True, entries=False)
 
 
+@pytest.mark.parametrize("beta_one", [False, True])
+def test_keys_at_the_edge_of_the_bound(dev, beta_one):
+    """The single-stream workload's shape (T=4096, nk=16, nv=32) with every key
+    scaled to |k|^2 = 1.9, so beta_t |k_t|^2 reaches 1.9 (with beta = 1: at the
+    edge of the domain beta |k|^2 <= rho < 2 in which ||T'|| <= 2 beta_max /
+    (2 - rho), here 20): the keys are passed as they are (no normalisation),
+    T' entries reach several units, and every chain is checked against the
+    oracle at the graded bars, intermediates of three chunks included."""
+    p = I.make_workload(2)
+    k = bf16_to_f64(p.k) * np.sqrt(1.9)
+    p.k = f32_to_bf16_bits(k.astype(np.float32))
+    kk = np.sum(bf16_to_f64(p.k) ** 2, axis=-1)
+    assert 1.85 < kk.min() and kk.max() < 1.95
+    if beta_one:
+        p.beta[:] = 1.0
+    dp = run(dev, p, flags=0)
+    w = check_problem(dp, p, chunked=True)
+    print(f"keys at |k|^2 = 1.9, beta one {beta_one}: {w}", flush=True)
+    assert_within(w, entries=False)
+    wc = check_chunks(dp, p, 0, [0, 31], [0, 32, 63])
+    print(wc, flush=True)
+    assert_within(wc, intermediates=True, entries=False)
+
+
 @pytest.mark.slow
 def test_l2norm_long_packed_sampled(dev):
     """The long packed workload's shape (T=65536, nv=48, conv layout) with raw

@@ -6,8 +6,8 @@ relative) and computes with it exactly.  These tests run the oracle's chunked
 form in float64 with only T' rounded, and show why the pair and not a single
 float16 (2^-11) is stored: with keys spread at random float16 would do, but
 with unit keys clustered around one direction and weak or no decay (inputs
-the method allows) float16 alone reaches the 1e-3 state bar, while the pair
-stays two orders of magnitude inside it.  The last test checks the bound on
+the method allows) float16 alone comes within reach of the 1e-3 state bar
+(over half of it), while the pair stays at least 20 times inside it.  The last test checks the bound on
 |T'| that makes the storage safe from overflow in the method's domain.
 """
 
