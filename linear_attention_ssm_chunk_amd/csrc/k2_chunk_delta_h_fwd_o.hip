@@ -19,21 +19,28 @@
 // fills the chip: few long chains get more workgroups each):
 //   * waves 0..S-1 (compute): one strip each for the whole pass.  The strip
 //     lives in MFMA accumulators; in the chain k order those registers are the
-//     B operand of K h and Q h directly, and so are the C tiles of
+//     B operand of K h (and of Q h), and so are the C tiles of
 //     R = V - e^G K h (for T' R) and of uc (for K^T uc and A uc): the
-//     dependent chain never leaves registers.  Step c runs chunk c's chain and
-//     state term diag(exp(G)) Q h, and finishes chunk c-1's output with A uc,
-//     whose scores were formed during step c-1;
-//   * waves S..S+3 (loaders), two pairs that take turns.  In step c the
-//     active pair stages chunk c+1 into the free half of a double-buffered
-//     LDS stage, from registers it filled two steps earlier, then fetches
-//     chunk c+3: role 0 the Q and K rows (1 KB per load), role 1 the T'
-//     fragments (bf16 hi + lo), the
-//     gate sums G (from which it forms the decays as it stages them; with q/k
-//     normalisation the row scales too) and V rows.  The idle pair works on chunk c, visible
-//     in the stage compute reads: role 1 reads the Q and K row fragments and
-//     forms the causal decayed scores A of chunk c on MFMA (for S = 4 role 0
-//     forms half of them); role 0 stores the output tile of chunk c-2.
+//     dependent chain never leaves registers.  Step c runs chunk c's chain;
+//     with S = 4 it also forms the state term diag(exp(G)) Q h and finishes
+//     chunk c-1's output with A uc, whose scores were formed during step c-1;
+//   * the loader waves, in two pairs that take turns.  In step c the active
+//     pair of each role stages chunk c+1 into the free half of a
+//     double-buffered LDS stage, from registers it filled two steps earlier,
+//     then fetches chunk c+3; the idle pair works on chunk c, already staged.
+//     With S = 4 (four loaders): role 0 fetches the Q and K rows (1 KB per
+//     load) and stores the output tile of chunk c-2; role 1 fetches the T'
+//     fragments (bf16 hi + lo), the gate sums G (from which it forms the
+//     decays as it stages them; with q/k normalisation the row scales too)
+//     and V rows; the idle waves of both roles form the causal decayed scores
+//     A of chunk c on MFMA, half each, for the compute waves.
+//     With S <= 2 (six loaders; two SIMDs hold no compute wave): role 1 on
+//     those SIMDs fetches T', G and V as above; its idle wave forms chunk c's
+//     scores and keeps them, and in step c+1 forms chunk c's output from the
+//     compute waves' bf16 h and bf16 uc, left in LDS; role 0 fetches the Q
+//     rows and stores the output tiles, role 2 the K rows.  After each
+//     barrier the Q- and K-row loaders wait before staging, so that the
+//     compute waves' first LDS reads of the step go first.
 //     The compute waves read K^T and their V tiles out of the row tiles with
 //     transposing LDS reads.
 // One barrier per chunk (and one after the last).  Entry states (when asked
@@ -42,8 +49,8 @@
 // lane holds 8-byte pieces of token rows; they are gathered per chunk in an
 // LDS tile and stored by a loader as whole row segments of the workgroup's
 // columns.
-// Every double-buffered region (stage, scores, output tile) is written in one
-// step and read in the next, and written again only after the barrier that
+// Every double-buffered region (stage, scores, h and uc tiles, output tile) is
+// written in one step and read in the next, and written again only after the barrier that
 // ends the reading step.
 // Precision: h is float32 between chunks; h, R and the decayed uc are split
 // into bf16 hi+lo for the products that feed the state (K is exact in bf16;
