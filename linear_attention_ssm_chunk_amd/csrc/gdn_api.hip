@@ -312,7 +312,7 @@ int validate_decode(const void *q, const void *k, const void *v, const float *g,
     return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
   if (nk <= 0 || nv <= 0) return fail(GDN_EINVAL, "head counts: nk=%d nv=%d must be positive", nk, nv);
   if (nv % nk != 0) return fail(GDN_EINVAL, "GQA grouping: nv=%d is not a multiple of nk=%d", nv, nk);
-  // one 64-lane workgroup per 32 columns of each v-head
+  // one 256-lane workgroup (four waves of 32 state rows) per v-head
   if (int64_t(nv) * (GDN_HEAD_DIM / 32) * 64 > kMaxWorkItems)
     return fail(GDN_EINVAL, "nv=%d is too large for the decode grid", nv);
   if (B <= 0 || B > 65535) return fail(GDN_EINVAL, "B=%d must be in 1..65535", B);
