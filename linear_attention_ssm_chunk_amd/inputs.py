@@ -61,6 +61,11 @@ WORKLOADS = {
             layout="contiguous", entry_states=True),
     4: dict(name="ragged_varlen_8seq", nseq=8, nk=16, nv=32, h0="normal", layout="varlen_table"),
     5: dict(name="long_packed_T65536", B=1, T=65536, nk=16, nv=48, h0="normal", layout="conv"),
+    # the prompt lengths of the prefills page 1 profiles (its tensor-core spine
+    # comment), at the head counts of workload 5: for setting the per-chunk
+    # spine cost beside the page's, not graded workloads
+    6: dict(name="page_prompt_T1193", B=1, T=1193, nk=16, nv=48, h0="zeros", layout="conv"),
+    7: dict(name="page_prompt_T4593", B=1, T=4593, nk=16, nv=48, h0="zeros", layout="conv"),
 }
 
 

@@ -376,6 +376,18 @@ def test_workload_every_chain(dev, index):
     assert_within(worst)
 
 
+@pytest.mark.parametrize("index", [6, 7])
+def test_page_prompt_shapes_in_full(dev, index):
+    """The prompt lengths page 1 profiles (1193 and 4593 tokens, ragged tails of
+    41 and 49 tokens) at nk=16, nv=48 in the packed conv layout: every chain
+    against the oracle's chunk form."""
+    p = I.make_workload(index)
+    dp = run(dev, p, layout="conv")
+    w = check_problem(dp, p, chunked=True)
+    print(f"workload {index}: {w}", flush=True)
+    assert_within(w)
+
+
 def test_ragged_workload_short_sequences_in_full(dev):
     """The ragged workload (8 sequences, state table) in the bench's launch:
     every head of each sequence shorter than 5000 tokens (6 of the 8; the two
