@@ -76,3 +76,38 @@ def test_noalloc_equals_prefill_ex_twice(flags):
         if ent is not None:
             assert torch.equal(ent, ref.region("s_entry"))
         assert_within(check_problem(got, p, seqs=[0], entries=False))
+
+
+@pytest.mark.gpu
+def test_noalloc_under_graph_capture():
+    """The call captured in a HIP graph (torch.cuda.graph) after one eager call
+    on the device: three replays, with the state reset and the outputs
+    cleared by eager work between them, each bit for bit equal to
+    gdn_prefill_ex on the same inputs (outputs, final states, entry states)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_ssm_chunk_amd.device import DeviceProblem, current_stream_handle
+    p = I.make_problem([700, 333], nk=2, nv=4, seed=83)
+    print(f"[gpu] noalloc graph lengths={p.lengths}", flush=True)
+    ref = DeviceProblem(p, flags=ENTRY, ragged=True)
+    ref.run()
+    torch.cuda.synchronize()
+    got = DeviceProblem(p, flags=ENTRY, ragged=True)
+    slots = int(p.cu_chunks[-1]) * p.nv
+    ent = torch.empty((slots, 128, 128), dtype=torch.bfloat16, device="cuda")
+    assert _call_noalloc(got, ent.data_ptr(), current_stream_handle()) == B.GDN_OK, B.gdn_last_error()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rc = _call_noalloc(got, ent.data_ptr(), current_stream_handle())
+    assert rc == B.GDN_OK, B.gdn_last_error()
+    for replay in range(3):
+        got.reset_state()
+        got.out.fill_(0)
+        ent.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(got.out, ref.out), replay
+        assert np.array_equal(got.state(), ref.state()), replay
+        assert torch.equal(ent, ref.region("s_entry")), replay
