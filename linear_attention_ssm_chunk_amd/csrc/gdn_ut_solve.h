@@ -1,6 +1,6 @@
 // gdn_ut_solve.h -- the per-chunk gate scan and UT solve, one wave per
-// (chunk, v-head), of chunk_cumsum_recompute_wu; the spine uses its exact
-// bf16 hi/lo split (SplitK).
+// (chunk, v-head), of chunk_cumsum_recompute_wu.  Its exact bf16 hi/lo split
+// (SplitK) has the same form as the spine's (split_tiles).
 //
 // Page "spark_model/layers/ops/ssm_gdn_a3.rs", doc comment of gdn_prefill_fla,
 // stage 1: the chunk-local cumulative log-gate gc and the WY/UT solves
