@@ -223,14 +223,20 @@ def test_rerun_is_byte_identical(dev):
     assert torch.equal(o1, dp.out) and torch.equal(h1, dp.h)
 
 
-def test_stages_in_order_equal_one_call(dev):
-    p = I.make_problem([190], nk=1, nv=2, seed=16)
-    a = run(dev, p)
-    b = dev(p)
+@pytest.mark.parametrize("flags,raw", [(0x1, False), (0x0, False), (0x3, True)])
+def test_stages_in_order_equal_one_call(dev, flags, raw):
+    """Stage 1 then stage 2 through gdn_prefill_stage_ex equal one
+    gdn_prefill_ex call bit for bit -- outputs, final states and the whole
+    scratch (intermediates, row scales, entry states) -- with and without
+    entry states and q/k normalisation."""
+    p = I.make_problem([190, 77], nk=2, nv=4, seed=16, raw_qk=raw)
+    a = run(dev, p, flags=flags, ragged=True)
+    b = dev(p, flags=flags, ragged=True)
     for st in (1, 2):
         b.run_stage(st)
     torch.cuda.synchronize()
     assert torch.equal(a.out, b.out) and torch.equal(a.h, b.h)
+    assert torch.equal(a.scratch, b.scratch)
 
 
 def test_split_resume_through_in_place_state(dev):
