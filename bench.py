@@ -246,9 +246,10 @@ def decode_bytes(B, nk, nv):
 def _oracle_decode_worker(args):
     w, workers, seconds = args
     from threadpoolctl import threadpool_limits
-    from oracle import gdn_recurrence, kv_head_map
+    from oracle import gdn_recurrence, kv_head_map, l2_normalize
     from linear_attention_ssm_chunk_amd.inputs import bf16_to_f64
     p = _SAMPLE_PROBLEM
+    raw = p.meta.get("raw_qk", False)
     kmap = kv_head_map(p.nk, p.nv)
     done = 0
     t0 = time.perf_counter()
@@ -257,8 +258,10 @@ def _oracle_decode_worker(args):
         while time.perf_counter() - t0 < seconds:
             i, h = chain % p.nseq, (chain // p.nseq) % p.nv
             kap = kmap[[h]]
-            gdn_recurrence(bf16_to_f64(p.q[i:i + 1][:, kap]), bf16_to_f64(p.k[i:i + 1][:, kap]),
-                           bf16_to_f64(p.v[i:i + 1][:, [h]]), p.g[i:i + 1][:, [h]].astype("float64"),
+            q, k = bf16_to_f64(p.q[i:i + 1][:, kap]), bf16_to_f64(p.k[i:i + 1][:, kap])
+            if raw:
+                q, k = l2_normalize(q), l2_normalize(k)
+            gdn_recurrence(q, k, bf16_to_f64(p.v[i:i + 1][:, [h]]), p.g[i:i + 1][:, [h]].astype("float64"),
                            p.beta[i:i + 1][:, [h]].astype("float64"), p.h0[i][[h]].astype("float64"))
             done += 1
             chain += workers
@@ -270,7 +273,9 @@ def bench_decode(args):
     global _SAMPLE_PROBLEM
     from linear_attention_ssm_chunk_amd import inputs as I
     sh = DECODE_SHAPE
-    p = I.make_problem([1] * sh["B"], sh["nk"], sh["nv"], seed=6)
+    raw = bool(args.raw_qk)
+    p = I.make_problem([1] * sh["B"], sh["nk"], sh["nv"], seed=6, raw_qk=raw)
+    p.meta["raw_qk"] = raw
     cpu = None
     if not args.no_cpu_baseline:
         _SAMPLE_PROBLEM = p
@@ -287,7 +292,8 @@ def bench_decode(args):
                           f"head-steps, wall {wall:.1f}s; tokens/s = head-steps/s / nv")}
     import torch
     from linear_attention_ssm_chunk_amd.device import DeviceProblem
-    dp = DeviceProblem(p, ragged=False)
+    # the decode takes the problem's q/k normalisation bit (GDN_OPT_L2NORM_QK with --raw-qk)
+    dp = DeviceProblem(p, ragged=False, flags=OPT_L2NORM_QK if raw else 0)
     warm_t0 = time.perf_counter()
     warm_steps = 0
     while warm_steps < args.warmup or time.perf_counter() - warm_t0 < WARMUP_MIN_S:
@@ -314,10 +320,11 @@ def bench_decode(args):
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "decode_B256", "B": sh["B"], "nk": sh["nk"], "nv": sh["nv"], "dk": 128, "dv": 128,
-                   "tokens_per_sequence": 1},
+                   "tokens_per_sequence": 1, "qk_normalised_in_kernels": raw},
         "roofline": {"bound": "hbm", "kernel": "recurrent_decode", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for_decode()},
+                     # the committed counters are of the call without normalisation
+                     "traffic": None if raw else traffic_for_decode()},
         "kernels": {"recurrent_decode": {"ms": round(ms_kernel, 4), "alg_bytes": by}},
         "cpu_baseline": cpu,
     }

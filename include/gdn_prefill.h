@@ -312,14 +312,25 @@ int gdn_varlen_check_host(int B, int T, const int32_t *cu_seqlens_host, const in
  *            table of B pointers to [nv][dk][dv], each entry 16-byte aligned
  *            as there; every entry is read), updated in place.
  *   out      bf16 [B][nv][dv], contiguous.
+ *   flags    (_ex) GDN_OPT_L2NORM_QK: q and k arrive unnormalised and the
+ *            kernel takes the step on k/|k| and q/|q| (per token and k-head;
+ *            a zero vector stays zero), as gdn_prefill_ex does with that
+ *            option, so a sequence prefilled with it decodes the same way.
+ *            No other bit is accepted (GDN_EINVAL).  gdn_decode passes 0.
  * dk = dv = 128; 1 <= B <= 65535; nv * 256 < 2^32 (work-items of the launch).  No scratch; one launch on `stream`, no synchronisation.
- * Returns GDN_OK or an error as gdn_prefill does; gdn_decode_validate runs the
- * same checks without touching the GPU.
+ * Returns GDN_OK or an error as gdn_prefill does; gdn_decode_validate(_ex)
+ * runs the same checks without touching the GPU.
  */
+int gdn_decode_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
+                  const gdn_strides *strides, unsigned flags, void *stream);
 int gdn_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
                void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
                const gdn_strides *strides, void *stream);
 
+int gdn_decode_validate_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                           void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk,
+                           int dv, const gdn_strides *strides, unsigned flags);
 int gdn_decode_validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
                         void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk,
                         int dv, const gdn_strides *strides);

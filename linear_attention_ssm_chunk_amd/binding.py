@@ -100,8 +100,12 @@ def _declare(L):
     dec = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, ctypes.POINTER(gdn_strides)]
     L.gdn_decode.argtypes = dec + [vp]
     L.gdn_decode.restype = i32
+    L.gdn_decode_ex.argtypes = dec + [u32, vp]
+    L.gdn_decode_ex.restype = i32
     L.gdn_decode_validate.argtypes = dec
     L.gdn_decode_validate.restype = i32
+    L.gdn_decode_validate_ex.argtypes = dec + [u32]
+    L.gdn_decode_validate_ex.restype = i32
     L.gdn_last_error.argtypes = []
     L.gdn_last_error.restype = ctypes.c_char_p
     return L
@@ -260,7 +264,23 @@ def gdn_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, 
     return rc
 
 
+def gdn_decode_ex(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides, flags, stream):
+    """gdn_decode with GDN_OPT_* flags (GDN_OPT_L2NORM_QK only).  Raises
+    GdnError on a nonzero return."""
+    args, keep = _decode_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides)
+    rc = lib().gdn_decode_ex(*args, int(flags), ctypes.c_void_p(int(stream)))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+    return rc
+
+
 def gdn_decode_validate(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides):
     """Return code of the decode's host validation (no exception)."""
     args, keep = _decode_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides)
     return lib().gdn_decode_validate(*args)
+
+
+def gdn_decode_validate_ex(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides, flags):
+    """Return code of gdn_decode_ex's host validation (no exception)."""
+    args, keep = _decode_args(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides)
+    return lib().gdn_decode_validate_ex(*args, int(flags))

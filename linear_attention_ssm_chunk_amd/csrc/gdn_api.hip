@@ -307,7 +307,10 @@ int scratch_on(int dev, void **out) {
 
 int validate_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
                     void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
-                    const gdn_strides *strides) {
+                    const gdn_strides *strides, unsigned flags) {
+  if (flags & ~unsigned(GDN_OPT_L2NORM_QK))
+    return fail(GDN_EINVAL, "flags=0x%x: the decode takes only GDN_OPT_L2NORM_QK (0x%x)", flags,
+                unsigned(GDN_OPT_L2NORM_QK));
   if (dk != GDN_HEAD_DIM || dv != GDN_HEAD_DIM)
     return fail(GDN_EUNSUPPORTED, "head size: dk=%d dv=%d, the kernels are built for dk = dv = 128", dk, dv);
   if (nk <= 0 || nv <= 0) return fail(GDN_EINVAL, "head counts: nk=%d nv=%d must be positive", nk, nv);
@@ -496,16 +499,22 @@ int gdn_varlen_check_host(int B, int T, const int32_t *cu_seqlens_host, const in
   return ok();
 }
 
+int gdn_decode_validate_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                           void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
+                           const gdn_strides *strides, unsigned flags) {
+  return validate_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides, flags);
+}
+
 int gdn_decode_validate(const void *q, const void *k, const void *v, const float *g, const float *beta,
                         void *h_state, int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv,
                         const gdn_strides *strides) {
-  return validate_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides);
+  return validate_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides, 0u);
 }
 
-int gdn_decode(const void *q, const void *k, const void *v, const float *g, const float *beta, void *h_state,
-               int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv, const gdn_strides *strides,
-               void *stream) {
-  int rc = validate_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides);
+int gdn_decode_ex(const void *q, const void *k, const void *v, const float *g, const float *beta, void *h_state,
+                  int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+                  unsigned flags, void *stream) {
+  int rc = validate_decode(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides, flags);
   if (rc != GDN_OK) return rc;
   gdn::Params p{};
   p.q = static_cast<const uint16_t *>(q);
@@ -523,9 +532,16 @@ int gdn_decode(const void *q, const void *k, const void *v, const float *g, cons
   p.T = 1;
   p.nk = nk;
   p.nv = nv;
+  p.opts = flags;
   const hipError_t e = gdn::launch_decode(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GDN_EHIP, "launch of recurrent_decode failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int gdn_decode(const void *q, const void *k, const void *v, const float *g, const float *beta, void *h_state,
+               int h_state_is_table, void *out, int B, int nk, int nv, int dk, int dv, const gdn_strides *strides,
+               void *stream) {
+  return gdn_decode_ex(q, k, v, g, beta, h_state, h_state_is_table, out, B, nk, nv, dk, dv, strides, 0u, stream);
 }
 
 const char *gdn_last_error(void) { return g_err; }

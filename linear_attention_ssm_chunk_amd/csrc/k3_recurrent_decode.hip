@@ -16,12 +16,17 @@
 // of this kernel.  (One wave per 32-column block, the four blocks of a head
 // in separate workgroups, moved 128-byte row pieces instead and ran 10 %
 // slower.)
+// With q/k normalisation (kNorm) the same exchange also sums |k|^2 and |q|^2
+// over the waves' rows; with sk = 1/|k|, sq = 1/|q| (0 for a zero vector) the
+// sums become sk h^T k, sq h^T q and sk sq k . q, and h takes sk k delta^T:
+// the step on k/|k| and q/|q|, the prefill's normalisation.
 #include "gdn_device.h"
 
 namespace gdn {
 
 constexpr int kDecWaves = 4; // waves per workgroup (one head): 32 rows each
 
+template <bool kNorm>
 __global__ __launch_bounds__(64 * kDecWaves) void recurrent_decode(Params p) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.x, i = blockIdx.y;
@@ -59,35 +64,64 @@ __global__ __launch_bounds__(64 * kDecWaves) void recurrent_decode(Params p) {
 
   // h^T k, h^T q and k . q over the wave's 32 rows, then over the waves
   f32x4 hk = zero4(), hq = zero4();
-  float kq = 0.f;
+  float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     hk += H[j] * kr[j];
     hq += H[j] * qr[j];
     kq += kr[j] * qr[j];
+    if (kNorm) {
+      kk += kr[j] * kr[j];
+      qq += qr[j] * qr[j];
+    }
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     hk[e] += __shfl_xor(hk[e], 32, 64);
     hq[e] += __shfl_xor(hq[e], 32, 64);
   }
-  kq += __shfl_xor(kq, 32, 64); // over the two row halves; the 32 column lanes hold the same sums
+  // over the two row halves; the 32 column lanes hold the same sums
+  kq += __shfl_xor(kq, 32, 64);
+  if (kNorm) {
+    kk += __shfl_xor(kk, 32, 64);
+    qq += __shfl_xor(qq, 32, 64);
+  }
   __shared__ f32x4 part[kDecWaves][2][32];
-  __shared__ float kqp[kDecWaves];
+  __shared__ float kqp[kDecWaves][3];
   if (lane < 32) {
     part[w][0][lane] = hk;
     part[w][1][lane] = hq;
   }
-  if (lane == 0) kqp[w] = kq;
+  if (lane == 0) {
+    kqp[w][0] = kq;
+    if (kNorm) {
+      kqp[w][1] = kk;
+      kqp[w][2] = qq;
+    }
+  }
   __syncthreads();
   hk = zero4();
   hq = zero4();
   kq = 0.f;
+  kk = 0.f;
+  qq = 0.f;
 #pragma unroll
   for (int u = 0; u < kDecWaves; ++u) {
     hk += part[u][0][lane & 31];
     hq += part[u][1][lane & 31];
-    kq += kqp[u];
+    kq += kqp[u][0];
+    if (kNorm) {
+      kk += kqp[u][1];
+      qq += kqp[u][2];
+    }
+  }
+  float sk = 1.f;
+  if (kNorm) {
+    sk = kk > 0.f ? rsqrtf(kk) : 0.f;
+    const float sq = qq > 0.f ? rsqrtf(qq) : 0.f;
+    hk *= sk;
+    hq *= sq;
+    kq *= sk * sq;
   }
 
   // delta for the lane's columns; v of this head
@@ -104,7 +138,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void recurrent_decode(Params p) {
   // h <- a h + k delta^T, written back in place
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    *reinterpret_cast<f32x4 *>(hp + (row0 + 2 * j) * kDim + col) = a * H[j] + kr[j] * delta;
+    *reinterpret_cast<f32x4 *>(hp + (row0 + 2 * j) * kDim + col) = a * H[j] + (sk * kr[j]) * delta;
 
   if (w == 0 && rsub == 0)
     *reinterpret_cast<u32x2 *>(p.out + (int64_t(i) * p.nv + h) * kDim + col) = pack4_bf16(o[0], o[1], o[2], o[3]);
@@ -112,7 +146,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void recurrent_decode(Params p) {
 
 hipError_t launch_decode(const Params &p, hipStream_t stream) {
   dim3 grid(unsigned(p.nv), p.B);
-  hipLaunchKernelGGL(recurrent_decode, grid, dim3(64 * kDecWaves), 0, stream, p);
+  if (p.opts & kOptNorm)
+    hipLaunchKernelGGL(recurrent_decode<true>, grid, dim3(64 * kDecWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL(recurrent_decode<false>, grid, dim3(64 * kDecWaves), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -146,11 +146,12 @@ class DeviceProblem:
         s = current_stream_handle() if stream is None else stream
         return B.gdn_prefill_stage_ex(stage, *self.args(), self.flags, s)
 
-    def decode_step(self, t, out=None, stream=None):
-        """One gdn_decode call on token t of every sequence (dense problems, all
-        of length T): the token pointers advance t rows and the row pitch
+    def decode_step(self, t, out=None, stream=None, flags=None):
+        """One gdn_decode_ex call on token t of every sequence (dense problems,
+        all of length T): the token pointers advance t rows and the row pitch
         becomes T rows, so sequence b's token t is decode row b.  Writes bf16
-        [B][nv][128] into ``out`` (default: ``self.dec_out``)."""
+        [B][nv][128] into ``out`` (default: ``self.dec_out``).  ``flags``
+        defaults to the problem's q/k normalisation bit."""
         if self.ragged:
             raise ValueError("decode steps need sequences of one length")
         if not 0 <= t < self.T:
@@ -162,10 +163,11 @@ class DeviceProblem:
         st, T = self.strides, self.T
         strides = B.gdn_strides(st.qk_row * T, st.v_row * T, st.gb_row * T)
         s = current_stream_handle() if stream is None else stream
-        return B.gdn_decode(self.q + 2 * t * st.qk_row, self.k + 2 * t * st.qk_row, self.v + 2 * t * st.v_row,
-                            self.g + 4 * t * st.gb_row, self.beta + 4 * t * st.gb_row, self.h_ptr,
-                            self.h_is_table, out.data_ptr(), self.nseq, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
-                            strides, s)
+        fl = self.flags & B.GDN_OPT_L2NORM_QK if flags is None else int(flags)
+        return B.gdn_decode_ex(self.q + 2 * t * st.qk_row, self.k + 2 * t * st.qk_row, self.v + 2 * t * st.v_row,
+                               self.g + 4 * t * st.gb_row, self.beta + 4 * t * st.gb_row, self.h_ptr,
+                               self.h_is_table, out.data_ptr(), self.nseq, self.nk, self.nv, HEAD_DIM, HEAD_DIM,
+                               strides, fl, s)
 
     # -- results ---------------------------------------------------------------
     def output(self):

@@ -264,6 +264,29 @@ def test_decode_validation_names_the_guard():
     assert decode_validate(nk=1, nv=nv, strides=B.gdn_strides(128, nv * 128, nv))[0] == B.GDN_OK
 
 
+def test_decode_flags_are_checked():
+    """gdn_decode_validate_ex accepts q/k normalisation and nothing else (an
+    entry-state bit means nothing for one token); gdn_decode_validate is the
+    call with no flags."""
+    a = decode_args()
+    args = (a["q"], a["k"], a["v"], a["g"], a["beta"], a["h_state"], a["h_state_is_table"], a["out"], a["B"],
+            a["nk"], a["nv"], a["dk"], a["dv"], a["strides"])
+    assert B.gdn_decode_validate_ex(*args, 0) == B.GDN_OK
+    assert B.gdn_decode_validate_ex(*args, B.GDN_OPT_L2NORM_QK) == B.GDN_OK
+    for bad in (B.GDN_OPT_ENTRY_STATES, B.GDN_OPT_ENTRY_STATES | B.GDN_OPT_L2NORM_QK, 0x4, 0x80000000):
+        assert B.gdn_decode_validate_ex(*args, bad) == B.GDN_EINVAL
+        assert "flags" in B.gdn_last_error() and "GDN_OPT_L2NORM_QK" in B.gdn_last_error()
+    # the other guards run as without flags
+    bad_nv = dict(a, nv=5)
+    args_bad = (bad_nv["q"], bad_nv["k"], bad_nv["v"], bad_nv["g"], bad_nv["beta"], bad_nv["h_state"], 0,
+                bad_nv["out"], bad_nv["B"], bad_nv["nk"], bad_nv["nv"], 128, 128, bad_nv["strides"])
+    assert B.gdn_decode_validate_ex(*args_bad, B.GDN_OPT_L2NORM_QK) == B.GDN_EINVAL
+    assert "GQA" in B.gdn_last_error()
+    with pytest.raises(B.GdnError) as e:
+        B.gdn_decode_ex(*args, B.GDN_OPT_ENTRY_STATES, 0)
+    assert e.value.code == B.GDN_EINVAL
+
+
 def test_decode_rejects_without_touching_the_gpu():
     a = decode_args(nv=5)
     with pytest.raises(B.GdnError) as e:

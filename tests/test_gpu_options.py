@@ -199,3 +199,96 @@ def test_offsets_past_T_are_skipped(dev):
     assert bool((dp.out[100:] == sentinel.to(dp.out.device)).all())
     assert bool((dp.out[:100] != sentinel.to(dp.out.device)).all())
     assert_within(check_problem(dp, p, seqs=[0]))
+
+
+# --------------------------------------------------------------------------
+# q/k normalisation in the decode step
+
+
+def _decode_steps(dp, steps):
+    outs = []
+    for t in range(steps):
+        dp.decode_step(t)
+        torch.cuda.synchronize()
+        outs.append(dp.dec_out.float().cpu().numpy())
+    return np.stack(outs)
+
+
+def _oracle_normalised(p):
+    """Oracle outputs [T][B][nv][dv] and final states on q, k normalised per
+    token (dense problems)."""
+    from oracle import gdn_recurrence
+    from parity import seq_arrays
+    T = p.lengths[0]
+    o = np.zeros((T, p.nseq, p.nv, 128))
+    hs = []
+    for i in range(p.nseq):
+        oi, hi, _ = gdn_recurrence(**seq_arrays(p, i, normalize=True))
+        o[:, i] = oi
+        hs.append(hi)
+    return o, np.stack(hs)
+
+
+def test_decode_l2norm_raw_steps(dev):
+    """Five decode steps of four sequences (GQA 3) on raw N(0, 1) q and k with
+    the option, among them a zero key row, a zero query row, and rows scaled
+    by 1e-6 and 1e4: outputs at every step and the final states against the
+    oracle on the normalised rows."""
+    p = I.make_problem([5] * 4, nk=1, nv=3, seed=59, raw_qk=True)
+    p.k[2] = 0   # sequence 0, token 2 (dense rows: sequence b, token t at 5b + t)
+    p.q[7] = 0   # sequence 1, token 2
+    p.k[11] = f32_to_bf16_bits(bf16_to_f64(p.k[11]).astype(np.float32) * np.float32(1e-6))
+    p.q[13] = f32_to_bf16_bits(bf16_to_f64(p.q[13]).astype(np.float32) * np.float32(1e4))
+    print("[gpu] decode raw q/k, 5 steps", flush=True)
+    dp = dev(p, ragged=False, flags=NORM)
+    out = _decode_steps(dp, 5)
+    o_ref, h_ref = _oracle_normalised(p)
+    st = dp.state().astype(np.float64)
+    o_err = float(np.abs(out - o_ref).max())
+    s_err = max(relfro(st[i, h], h_ref[i, h]) for i in range(p.nseq) for h in range(p.nv))
+    print(f"decode raw q/k: o_maxabs={o_err:.3g} state_relfro={s_err:.3g}", flush=True)
+    assert o_err <= 2e-2 and s_err <= 1e-5
+
+
+def test_decode_l2norm_on_prenormalised_inputs(dev):
+    """q and k of the default recipe (unit length within bf16 rounding): the
+    decode with the option matches the oracle that normalises them once more,
+    and differs from the decode without it only by that rounding."""
+    p = I.make_problem([3] * 5, nk=2, nv=4, seed=60)
+    print("[gpu] decode unit q/k with and without the option", flush=True)
+    a = dev(p, ragged=False, flags=0)
+    b = dev(p, ragged=False, flags=NORM)
+    out_a, out_b = _decode_steps(a, 3), _decode_steps(b, 3)
+    o_ref, h_ref = _oracle_normalised(p)
+    st = b.state().astype(np.float64)
+    assert np.abs(out_b - o_ref).max() <= 2e-2
+    assert max(relfro(st[i, h], h_ref[i, h]) for i in range(p.nseq) for h in range(p.nv)) <= 1e-5
+    assert np.abs(out_a - out_b).max() <= 2e-2
+    assert relfro(st, a.state().astype(np.float64)) <= 2e-3
+
+
+def test_prefill_then_decode_l2norm(dev):
+    """A prefill of 130 raw tokens with q/k normalisation (a ragged chunk
+    tail) leaves the state in place; token 131 decoded from it with the option
+    matches the oracle over all 131 normalised tokens."""
+    from oracle import gdn_recurrence
+    from parity import seq_arrays
+    T = 131
+    full = I.make_problem([T] * 2, nk=2, nv=4, seed=61, raw_qk=True)
+    rows = np.concatenate([np.arange(i * T, i * T + T - 1) for i in range(2)])
+    last = np.array([i * T + T - 1 for i in range(2)])
+    pre = I.Problem([T - 1] * 2, full.nk, full.nv, full.q[rows], full.k[rows], full.v[rows], full.g[rows],
+                    full.beta[rows], full.h0.copy(), full.seed)
+    one = I.Problem([1] * 2, full.nk, full.nv, full.q[last], full.k[last], full.v[last], full.g[last],
+                    full.beta[last], full.h0.copy(), full.seed)
+    dp = run(dev, pre, flags=NORM)
+    dd = dev(one, ragged=False, flags=NORM)
+    dd.h.copy_(dp.h)  # the prefill's final state, in place for the next token
+    dd.decode_step(0)
+    torch.cuda.synchronize()
+    out = dd.dec_out.float().cpu().numpy()
+    st = dd.state().astype(np.float64)
+    for i in range(2):
+        o_ref, h_ref, _ = gdn_recurrence(**seq_arrays(full, i, normalize=True))
+        assert np.abs(out[i] - o_ref[-1]).max() <= 2e-2
+        assert max(relfro(st[i, h], h_ref[h]) for h in range(full.nv)) <= 1e-3
