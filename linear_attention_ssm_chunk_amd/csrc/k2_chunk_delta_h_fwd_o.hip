@@ -28,14 +28,15 @@
 //     pair of each role stages chunk c+1 into the free half of a
 //     double-buffered LDS stage, from registers it filled two steps earlier,
 //     then fetches chunk c+3; the idle pair works on chunk c, already staged.
-//     With S = 4 (four loaders): role 0 fetches the Q rows (1 KB per load)
-//     and stores the output tile of chunk c-2; role 1 fetches the K rows, the
-//     T' fragments (bf16 hi + lo), the gate sums G (from which it forms the
-//     decays as it stages them; with q/k normalisation the row scales too)
-//     and V rows; the idle waves of both roles form the causal decayed scores
-//     A of chunk c on MFMA, half each, for the compute waves.  (With the K
-//     rows on role 0 as well, that wave's loads were the longest part of its
-//     step: the ragged workload's spine ran 3.5 % slower.)
+//     With S = 4 (four loaders): role 0 fetches the Q rows and K rows 0..31
+//     (1 KB per load) and stores the output tile of chunk c-2; role 1 fetches
+//     K rows 32..63, the T' fragments (bf16 hi + lo), the gate sums G (from
+//     which it forms the decays as it stages them; with q/k normalisation the
+//     row scales too) and V rows; the idle waves of both roles form the causal
+//     decayed scores A of chunk c on MFMA, half each, for the compute waves.
+//     (All K rows on role 0, that wave's loads were the longest part of its
+//     step, and the ragged workload's spine ran 7 % slower; all on role 1,
+//     the batched workload's ran 2 % slower.)
 //     With S <= 2 (six loaders; two SIMDs hold no compute wave): role 1 on
 //     those SIMDs fetches T', G and V as above; its idle wave forms chunk c's
 //     scores and keeps them, and in step c+1 forms chunk c's output from the
@@ -234,9 +235,9 @@ __global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chun
     // Loader li = wave - S belongs to pair li % 2.  Waves are dealt to the four
     // SIMDs in turn, so for S <= 2 loaders li = 0, 1 sit on SIMDs without a
     // compute wave: they take role 1 (T', V, gate sums; the score products and,
-    // with kOL, the output; the K rows for S = 4); role 0 (Q rows; the output
-    // stores) shares a SIMD with a compute wave; with kOL role 2 (the K rows)
-    // sits beside a role-1 wave.  For S = 4 every SIMD holds one compute wave
+    // with kOL, the output; half the K rows for S = 4); role 0 (Q rows, and
+    // half the K rows for S = 4; the output stores) shares a SIMD with a
+    // compute wave; with kOL role 2 (the K rows) sits beside a role-1 wave.  For S = 4 every SIMD holds one compute wave
     // and one loader.
     const int li = wave - kStrips;
     const int pair = li & 1; // stages chunks c with c % 2 == pair
@@ -316,10 +317,10 @@ __global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chun
         for (int kb = 0; kb < 2; ++kb)
           if ((mask & (1 << mt)) && 2 * kb <= mt) dst[tri_frag(mt, kb) * 64 + lane] = A[tri_frag(mt, kb)];
     };
-    // S = 4: the 64 Q or K rows of chunk c (the k-head's 256 bytes of each
-    // token row), rx[j] = row 4j + lane/16, bf16 8 (lane%16) .. +7, and their
-    // place in a row tile of the stage
-    auto fetch_rows = [&](const uint16_t *base, int c, u32x4 (&rx)[16]) __attribute__((always_inline)) {
+    // S = 4: the Q or K rows 4 j0 .. 4 j1 - 1 of chunk c (the k-head's 256
+    // bytes of each token row), rx[j] = row 4j + lane/16, bf16 8 (lane%16)
+    // .. +7, and their place in a row tile of the stage
+    auto fetch_rows = [&](const uint16_t *base, int c, u32x4 (&rx)[16], int j0, int j1) __attribute__((always_inline)) {
       const int nn = min(kChunk, s.len - c * kChunk);
       // chunk bases are wave-uniform; a lane adds a 32-bit offset (row
       // pitches are bounded so that 64 rows stay below 2^31 bytes)
@@ -328,15 +329,17 @@ __global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chun
       const uint32_t pitch = uint32_t(p.qk_row) * 2u;
 #pragma unroll
       for (int jr = 0; jr < 16; ++jr) {
+        if (jr < j0 || jr >= j1) continue;
         // rows past the sequence end repeat its last row: they only reach
         // rows of products that are never stored, or meet zero rows of T'
         const uint32_t off = uint32_t(min(4 * jr + nrow, nn - 1)) * pitch + 16u * piece;
         rx[jr] = *reinterpret_cast<const u32x4 *>(src + off);
       }
     };
-    auto stash_rows = [&](u32x4 *tile, const u32x4 (&rx)[16]) __attribute__((always_inline)) {
+    auto stash_rows = [&](u32x4 *tile, const u32x4 (&rx)[16], int j0, int j1) __attribute__((always_inline)) {
 #pragma unroll
-      for (int jr = 0; jr < 16; ++jr) tile[row_slot(4 * jr + nrow, piece)] = rx[jr];
+      for (int jr = 0; jr < 16; ++jr)
+        if (jr >= j0 && jr < j1) tile[row_slot(4 * jr + nrow, piece)] = rx[jr];
     };
     GDN_STAMP_DECL;
     if (role != 1) {
@@ -347,14 +350,16 @@ __global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chun
       constexpr int kOps = 1;
       const bool doQ = !kOL || role == 0;
       u32x4 rx[kOps][16]; // rx[o][j] = operand row 4j + lane/16, bf16 8 (lane%16) .. +7
-      // At S = 4 (Q rows only) through the row helpers; with kOL through the
-      // form below.  Both issue the same loads and stores, but the compiler
+      u32x4 kx[16];       // S = 4: K rows 0..31
+      // At S = 4 (the Q rows and K rows 0..31) through the row helpers; with
+      // kOL through the form below.  Both issue the same loads and stores, but the compiler
       // schedules each kernel's address arithmetic differently, and these are
       // the pairings measured fastest (the other way round: 2 % slower at
       // S <= 2, 3 % on the ragged workload at S = 4).
       auto fetch = [&](int c) __attribute__((always_inline)) {
         if constexpr (!kOL) {
-          fetch_rows(p.q, c, rx[0]);
+          fetch_rows(p.q, c, rx[0], 0, 16);
+          fetch_rows(p.k, c, kx, 0, 8);
           return;
         }
         const int nn = min(kChunk, s.len - c * kChunk);
@@ -375,7 +380,8 @@ __global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chun
       };
       auto stash = [&](Stage &S) __attribute__((always_inline)) {
         if constexpr (!kOL) {
-          stash_rows(S.qr, rx[0]);
+          stash_rows(S.qr, rx[0], 0, 16);
+          stash_rows(S.kr, kx, 0, 8);
           return;
         }
         u32x4 *dst[2] = {doQ ? S.qr : S.kr, S.kr};
@@ -438,10 +444,10 @@ __global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chun
     u32x4 tx[2 * kTpFrags];  // T' as fetched and staged: bf16 hi (f), lo (6 + f)
     float gg = 0.f, skv = 1.f, sqv = 1.f;
     u32x4 vx[kVPieces];
-    u32x4 kx[16]; // S = 4: the K rows
+    u32x4 kx[16]; // S = 4: K rows 32..63
     auto fetch = [&](int c) __attribute__((always_inline)) {
       const int64_t sl = slot_of(p, s, h, c);
-      if constexpr (!kOL) fetch_rows(p.k, c, kx);
+      if constexpr (!kOL) fetch_rows(p.k, c, kx, 8, 16);
       const char *tsrc = reinterpret_cast<const char *>(p.tp) + sl * kTpBytes;
 #pragma unroll
       for (int part = 0; part < 2; ++part)
@@ -472,7 +478,7 @@ __global__ __launch_bounds__((kStrips + loader_waves<kStrips>()) * 64) void chun
     // the chunk's per-token factors from G (rows past the sequence end repeat
     // the last G, so lane 63 holds G_n)
     auto stash = [&](Stage &S) __attribute__((always_inline)) {
-      if constexpr (!kOL) stash_rows(S.kr, kx);
+      if constexpr (!kOL) stash_rows(S.kr, kx, 8, 16);
 #pragma unroll
       for (int f = 0; f < 2 * kTpFrags; ++f) S.tp[f * 64 + lane] = tx[f];
       const float Gn = __shfl(gg, kChunk - 1, 64);
