@@ -374,8 +374,9 @@ COMPUTE_SECTIONS = {  # mark k closes the section that began at mark k-1 (k2_chu
 # loader roles: (name, what marks 1, 2, 3 close in a step where the pair stages
 # the next chunk ("active"), what mark 3 closes in the other steps ("idle"))
 LOADER_ROLES = {
-    (4, 0): ("Q rows; output stores; score rows 0 and 3", "stage", "issue fetch", "-", "output stores, scores"),
-    (4, 1): ("K rows, T', V, gate factors; score rows 1 and 2", "stage", "issue fetch", "-", "scores"),
+    (4, 0): ("Q rows, K rows 0..31; output stores; score rows 0 and 3", "stage", "issue fetch", "-",
+             "output stores, scores"),
+    (4, 1): ("K rows 32..63, T', V, gate factors; score rows 1 and 2", "stage", "issue fetch", "-", "scores"),
     (2, 0): ("Q rows; output stores", "delay and stage", "issue fetch", "-", "delay and output stores"),
     (2, 1): ("T', V, gate factors; scores; output", "stage", "issue fetch", "output", "scores"),
     (2, 2): ("K rows", "delay and stage", "issue fetch", "-", "delay"),
