@@ -227,14 +227,14 @@ def test_two_streams_at_once(dev):
     """Two calls with their own outputs, states and scratch, enqueued back to
     back on two streams so that their kernels may run at the same time (which
     the header allows): each equals the same call run alone, bit for bit,
-    outputs, final states and entry states, on three rounds."""
+    outputs, final states and entry states, three times over."""
     pa = I.make_problem([4096], nk=2, nv=4, seed=91)
     pb = I.make_problem([1500, 700, 64], nk=4, nv=12, seed=92)  # one and two strips per workgroup
     refs = [run(dev, p, ragged=(p is pb)) for p in (pa, pb)]
     pair = [dev(p, ragged=(p is pb)) for p in (pa, pb)]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    for rnd in range(3):
-        print(f"[gpu] two streams, round {rnd}", flush=True)
+    for rep in range(3):
+        print(f"[gpu] two streams, pass {rep}", flush=True)
         for d in pair:
             d.reset_state()
             d.out.fill_(0)
@@ -244,8 +244,8 @@ def test_two_streams_at_once(dev):
             d.run(s.cuda_stream)
         torch.cuda.synchronize()
         for d, r in zip(pair, refs):
-            assert torch.equal(d.out, r.out) and torch.equal(d.h, r.h), rnd
-            assert torch.equal(d.region("s_entry"), r.region("s_entry")), rnd
+            assert torch.equal(d.out, r.out) and torch.equal(d.h, r.h), rep
+            assert torch.equal(d.region("s_entry"), r.region("s_entry")), rep
 
 
 @pytest.mark.parametrize("flags,raw", [(0x1, False), (0x0, False), (0x3, True)])
