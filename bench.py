@@ -21,7 +21,8 @@ roofline: the dominant kernel's irreducible bytes per launch -- what the
 method must move at least, whatever the implementation: q and k once per
 k-head, v, the output, the entry states where the workload asks for them, and
 the state read and written -- over its average launch time, timed live with
-HIP events on the launch stream; "whole_step" gives the same for the whole
+HIP events on the launch stream (timing-only events, without the
+system-scope fence: "timing_events"); "whole_step" gives the same for the whole
 step (g and beta added).  The implementation's own byte model (its
 intermediates included) is reported beside it as "impl_*".
 traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, read
@@ -515,6 +516,64 @@ def stream_ceiling(args):
     print(json.dumps(out), flush=True)
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it skips the system-scope cache write-back and invalidation that
+    a default event performs (and that slows the kernel after it).  The times
+    are read only after a device synchronisation.  The HIP runtime is the one
+    torch has loaded (the process holds one copy, found by its mapped path)."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            hip = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [vp, vp]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            hip.hipEventDestroy.argtypes = [vp]
+            for fn in (hip.hipEventCreateWithFlags, hip.hipEventRecord, hip.hipEventElapsedTime, hip.hipEventDestroy):
+                fn.restype = ctypes.c_int
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ctypes = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: error {rc}")
+
+    def record(self, stream):
+        rc = self._runtime().hipEventRecord(self.ev, self._ctypes.c_void_p(int(stream)))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: error {rc}")
+
+    def elapsed_time(self, end):
+        ms = self._ctypes.c_float()
+        rc = self._runtime().hipEventElapsedTime(self._ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: error {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -526,6 +585,8 @@ def main():
                     help="emit the per-chunk entry states: auto = where the workload asks for them")
     ap.add_argument("--raw-qk", action="store_true",
                     help="draw q and k unnormalised and have the kernels normalise them (GDN_OPT_L2NORM_QK)")
+    ap.add_argument("--events", choices=("nofence", "torch"), default="nofence",
+                    help="timing events: HIP events without the system-scope fence (default), or torch's")
     ap.add_argument("--decode", action="store_true",
                     help="measure the recurrent decode step (gdn_decode) on a batch of 256 sequences instead")
     ap.add_argument("--section-stamps", action="store_true",
@@ -604,15 +665,21 @@ def main():
     warm_ms = (time.perf_counter() - warm_t0) * 1e3
 
     stages = sorted(KERNELS)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream().cuda_stream  # the stream the stages are launched on
+    if args.events == "torch":
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+        rec = lambda e: e.record()  # noqa: E731
+    else:
+        ev = [[TimingEvent() for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+        rec = lambda e: e.record(stream)  # noqa: E731
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         e = ev[s]
-        e[0].record()
+        rec(e[0])
         for st in stages:
             dp.run_stage(st)
-            e[st].record()
+            rec(e[st])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -663,6 +730,7 @@ def main():
                      "impl_bytes_per_launch": by[dom],
                      "impl_frac": round(gbps(by[dom], per[dom]) / HBM_PEAK_GBS, 4)},
         "kernels": kernels,
+        "timing_events": "HIP, no system-scope fence" if args.events == "nofence" else "torch (default HIP events)",
         "whole_step": {"io_bytes": io_total, "io_GBps": round(gbps(io_total, ms_per_step), 1),
                        "io_frac": round(gbps(io_total, ms_per_step) / HBM_PEAK_GBS, 4),
                        "impl_bytes": total_bytes, "impl_GBps": round(gbps(total_bytes, ms_per_step), 1),
