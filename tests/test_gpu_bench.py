@@ -55,7 +55,10 @@ def test_prefill_line_with_the_oracle_leg():
     check_common(d, 3, 2)
     assert d["dtype"] == "bf16"
     cfg = d["config"]
-    assert abs(d["value"] - cfg["n_tokens"] / (d["ms_per_step"] / 1e3)) <= 1e-3 * d["value"] + 1.0
+    # ms_per_step is printed to 4 decimals: the rate recomputed from it may be
+    # off by that rounding, relative 5e-5 / ms_per_step
+    tol = d["value"] * 6e-5 / d["ms_per_step"] + 1.0
+    assert abs(d["value"] - cfg["n_tokens"] / (d["ms_per_step"] / 1e3)) <= tol
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["unit"] == "tokens/s"
     assert cpu["cores"] >= 1 and cpu["host_cores"] >= 1 and isinstance(cpu["sample"], str)
